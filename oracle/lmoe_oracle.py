@@ -1,0 +1,193 @@
+"""Plain, slow CPU oracle of the LatentMoE layer forward pass.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the product path never
+imports this module.
+
+Definition followed (page "Nemotron 3 Ultra 架构深度拆解报告", CH5 §5.6,
+"7 步数据流", Steps 1-7, with the router moved onto the latent as the
+same page's summary (CH0) and the Super overview page ("NVIDIA Nemotron 3
+Super 技术解读", §2.2) describe it):
+
+    z      = x W1^T                                   fc1_latent_proj  (Step 5)
+    l      = z Wg^T                     (float32)     router gate      (Step 1)
+    s      = sigmoid(l)                 (float32)                      (Step 2)
+    b      = s + beta                   (float32)     selection only   (Step 2)
+    I_t    = the K largest b_t (single group)                          (Step 3)
+    w_t    = rho * s_t[I_t] / (sum s_t[I_t] + 1e-20)                   (Step 4)
+    E_e(u) = relu(u Wup[e]^T)^2 Wdn[e]^T  (non-gated MLP)              (Step 6, §5.1)
+    r_t    = sum_k w_t,k E_{I_t,k}(z_t)                                (Step 6)
+    y_t    = r_t W2^T + relu(x_t Wsu^T)^2 Wsd^T                        (Step 7)
+
+Weights are stored out x in, so ``linear(u, W) = u @ W.T`` (§5.1: expert
+tensors are (num_experts, out_dim, in_dim)); no layer has a bias (§2.3.4).
+
+Readings taken where the pages are silent or disagree:
+
+* the router reads the float32 latent z (the gate upcasts its input to fp32,
+  Step 1), not a bf16-rounded copy;
+* relu^2(u) = max(u, 0)^2 for the experts and the shared expert;
+* ties between equal biased scores go to the lower expert index, and the K
+  selected experts are reported in ascending expert id (``topk`` is called
+  with ``sorted=False``, so the order carries no meaning);
+* the 1e-20 is added to the float32 sum before dividing, then the quotient is
+  multiplied by rho (Step 4 order);
+* single routing group: the group score step of §5.5 is a no-op.
+
+Parity pins (tests/test_oracle_pins.py): a hand-derived micro example
+(tests/golden/worked_example_micro.json), brute-force subset enumeration for
+the top-K, closed-form sigmoid values, exact integer GEMMs, the dense
+"every expert on every token" formulation, and the invariants sum(w) = rho,
+K = 1, K = E, x = 0, Wup = 0, identical experts, token-order equivariance and
+the page's parameter/FLOP accounting.  No function here is unpinned.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+F32 = np.float32
+F64 = np.float64
+
+
+@dataclass(frozen=True)
+class OracleConfig:
+    """Layer sizes, named after the model's config keys (page
+    "Nemotron-3-Labs-Ultra-Math-SFT" article, 核心配置速查表)."""
+
+    hidden_size: int
+    moe_latent_size: int
+    n_routed_experts: int
+    num_experts_per_tok: int
+    moe_intermediate_size: int
+    moe_shared_expert_intermediate_size: int
+    routed_scaling_factor: float = 5.0
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Exact value of bfloat16 bit patterns (uint16) as float64.
+
+    A bfloat16 is the upper 16 bits of an IEEE float32, so the value is the
+    float32 whose high half is ``bits`` and whose low half is zero."""
+    u = np.asarray(bits, dtype=np.uint16)
+    return (u.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(F64)
+
+
+def latent_projection(x: np.ndarray, W1: np.ndarray) -> np.ndarray:
+    """fc1_latent_proj: z = x W1^T, float64 (Step 5)."""
+    return np.asarray(x, F64) @ np.asarray(W1, F64).T
+
+
+def router_scores(z32: np.ndarray, Wg: np.ndarray):
+    """Router gate and sigmoid (Steps 1-2), in float32 as the page fixes.
+
+    The logits are the float64 dot products of the float32 latent with the
+    float32 gate rows, rounded once to float32.  The sigmoid 1/(1+e^-l) is
+    evaluated in float64 from that float32 logit and rounded once."""
+    z32 = np.asarray(z32, F32)
+    Wg = np.asarray(Wg, F32)
+    logits = (z32.astype(F64) @ Wg.astype(F64).T).astype(F32)
+    s = (1.0 / (1.0 + np.exp(-logits.astype(F64)))).astype(F32)
+    return logits, s
+
+
+def select_experts(s: np.ndarray, beta: np.ndarray, k: int):
+    """Top-K selection on the biased score (Steps 2-3, single group).
+
+    b = s + beta in float32.  For each token the experts are ranked by b
+    descending, equal b ranked by expert index ascending; the first ``k`` are
+    kept and returned in ascending expert id.  ``gap`` is the difference
+    between the k-th and the (k+1)-th ranked biased scores (+inf if k = E),
+    i.e. how close the token is to a different selection."""
+    s = np.asarray(s, F32)
+    b = (s + np.asarray(beta, F32)[None, :]).astype(F32)
+    t, e = b.shape
+    expert_ids = np.broadcast_to(np.arange(e), b.shape)
+    ranked = np.lexsort((expert_ids, -b), axis=-1)
+    idx = np.sort(ranked[:, :k], axis=1)
+    if k < e:
+        bk = np.take_along_axis(b, ranked[:, k - 1:k], 1)[:, 0].astype(F64)
+        bk1 = np.take_along_axis(b, ranked[:, k:k + 1], 1)[:, 0].astype(F64)
+        gap = bk - bk1
+    else:
+        gap = np.full(t, np.inf)
+    return idx, b, gap
+
+
+def renormalize(s: np.ndarray, idx: np.ndarray, rho: float) -> np.ndarray:
+    """Routing weights (Step 4): gather the unbiased scores of the selected
+    experts, divide by (their float32 sum + 1e-20), multiply by rho.
+
+    The sum runs over the selected experts in ascending expert id, one
+    float32 addition at a time."""
+    sel = np.take_along_axis(np.asarray(s, F32), idx, 1).astype(F32)
+    acc = np.zeros(sel.shape[0], F32)
+    for j in range(sel.shape[1]):
+        acc = (acc + sel[:, j]).astype(F32)
+    denom = (acc + F32(1e-20)).astype(F32)
+    return ((sel / denom[:, None]).astype(F32) * F32(rho)).astype(F32)
+
+
+def expert_mlp(u: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """Non-gated relu^2 MLP, up -> act -> down (§5.1; Step 6), float64."""
+    h = np.maximum(np.asarray(u, F64) @ np.asarray(w_up, F64).T, 0.0) ** 2
+    return h @ np.asarray(w_down, F64).T
+
+
+def routed_experts(z: np.ndarray, idx: np.ndarray, w: np.ndarray,
+                   expert_up, expert_down) -> np.ndarray:
+    """Step 6: loop over the experts that received tokens, run each on its
+    tokens' latent rows, weight by the routing weight and add into the
+    token's row.
+
+    ``expert_up[e]`` / ``expert_down[e]`` return bfloat16 bit patterns
+    (uint16) of shape [F, R] / [R, F]; they are upcast one expert at a time.
+    Experts are visited in ascending id, so each token accumulates its
+    contributions in ascending expert order."""
+    z = np.asarray(z, F64)
+    r = np.zeros_like(z)
+    for e in np.unique(idx):
+        tok, pos = np.nonzero(idx == e)
+        o = expert_mlp(z[tok], bf16_bits_to_f64(expert_up[int(e)]),
+                       bf16_bits_to_f64(expert_down[int(e)]))
+        r[tok] += np.asarray(w, F64)[tok, pos][:, None] * o
+    return r
+
+
+def latent_up_projection(r: np.ndarray, W2: np.ndarray) -> np.ndarray:
+    """fc2_latent_proj: r W2^T, float64 (Step 7)."""
+    return np.asarray(r, F64) @ np.asarray(W2, F64).T
+
+
+def shared_expert(x: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """The shared expert on the un-projected input (Step 7), relu^2 MLP."""
+    return expert_mlp(x, w_up, w_down)
+
+
+def forward(x_bits, weights, cfg: OracleConfig, forced_idx=None) -> dict:
+    """Whole layer forward for the rows of ``x_bits`` (bf16 bits, [T, D]).
+
+    ``weights`` has attributes fc1_latent, router, router_bias, expert_up,
+    expert_down, fc2_latent, shared_up, shared_down (bf16 bits except the
+    float32 router and router_bias; expert_up/expert_down indexable by
+    expert id).  ``forced_idx`` ([T, K] ascending ids) replaces the
+    selection; it is used to re-evaluate tokens whose selection is within
+    rounding of a tie.  Returns y (float64) and the intermediate values."""
+    k = cfg.num_experts_per_tok
+    x = bf16_bits_to_f64(x_bits)
+    z = latent_projection(x, bf16_bits_to_f64(weights.fc1_latent))
+    z32 = z.astype(F32)
+    logits, s = router_scores(z32, weights.router)
+    idx, b, gap = select_experts(s, weights.router_bias, k)
+    if forced_idx is not None:
+        idx = np.sort(np.asarray(forced_idx, np.int64), axis=1)
+    w = renormalize(s, idx, cfg.routed_scaling_factor)
+    r = routed_experts(z, idx, w, weights.expert_up, weights.expert_down)
+    y_routed = latent_up_projection(r, bf16_bits_to_f64(weights.fc2_latent))
+    y_shared = shared_expert(x, bf16_bits_to_f64(weights.shared_up),
+                             bf16_bits_to_f64(weights.shared_down))
+    counts = np.bincount(idx.ravel(), minlength=cfg.n_routed_experts)
+    return dict(y=y_routed + y_shared, y_routed=y_routed, y_shared=y_shared,
+                z=z, z32=z32, logits=logits, s=s, b=b, idx=idx, w=w, gap=gap,
+                r=r, counts=counts)

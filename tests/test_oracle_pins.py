@@ -1,0 +1,344 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself:
+a hand-derived worked example, brute-force enumeration, closed forms, exact
+integer arithmetic, an independent (dense) formulation and invariants of
+the definition.  CPU only."""
+
+import itertools
+import json
+import math
+import os
+from types import SimpleNamespace
+
+import numpy as np
+import pytest
+import torch
+
+import lmoe_inputs as li
+import oracle
+from oracle import lmoe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def exact_bf16_bits(a) -> np.ndarray:
+    """bf16 bit patterns of values that bfloat16 represents exactly."""
+    f = np.asarray(a, np.float32)
+    u = f.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0), "value not exact in bfloat16"
+    return (u >> 16).astype(np.uint16)
+
+
+def micro_case():
+    g = json.load(open(os.path.join(GOLDEN, "worked_example_micro.json")))
+    sh = g["shape"]
+    cfg = O.OracleConfig(sh["hidden_size"], sh["moe_latent_size"], sh["n_routed_experts"],
+                         sh["num_experts_per_tok"], sh["moe_intermediate_size"],
+                         sh["moe_shared_expert_intermediate_size"], sh["routed_scaling_factor"])
+    ln3 = math.log(3.0)
+    w = SimpleNamespace(
+        fc1_latent=exact_bf16_bits(g["fc1_latent"]),
+        router=(np.asarray(g["router_ln3"], np.float64) * ln3).astype(np.float32),
+        router_bias=np.asarray(g["router_bias"], np.float32),
+        expert_up=exact_bf16_bits(g["expert_up"]),
+        expert_down=exact_bf16_bits(g["expert_down"]),
+        fc2_latent=exact_bf16_bits(g["fc2_latent"]),
+        shared_up=exact_bf16_bits(g["shared_up"]),
+        shared_down=exact_bf16_bits(g["shared_down"]),
+    )
+    return g, cfg, exact_bf16_bits(g["x"]), w
+
+
+def check_micro(out, exp):
+    np.testing.assert_allclose(out["z"], exp["z"], rtol=0, atol=0)
+    np.testing.assert_allclose(out["s"], exp["s"], rtol=1e-6)
+    np.testing.assert_array_equal(out["idx"], exp["idx"])
+    np.testing.assert_allclose(out["gap"], exp["gap"], rtol=1e-5)
+    np.testing.assert_allclose(out["w"], exp["w"], rtol=1e-6)
+    np.testing.assert_allclose(out["r"], exp["r"], rtol=1e-6)
+    np.testing.assert_allclose(out["y_shared"], exp["y_shared"], rtol=0, atol=0)
+    np.testing.assert_allclose(out["y"], exp["y"], rtol=1e-6)
+
+
+def test_worked_example_micro():
+    g, cfg, x, w = micro_case()
+    check_micro(O.forward(x, w, cfg), g["expected"])
+
+
+# Plausible mistakes, planted in the oracle on the CPU: each must break the
+# hand-derived example, which shows the example pins that part.
+def _relu_not_squared(u, w_up, w_down):
+    h = np.maximum(np.asarray(u, np.float64) @ np.asarray(w_up, np.float64).T, 0.0)
+    return h @ np.asarray(w_down, np.float64).T
+
+
+def _up_transposed(u, w_up, w_down):
+    h = np.maximum(np.asarray(u, np.float64) @ np.asarray(w_up, np.float64), 0.0) ** 2
+    return h @ np.asarray(w_down, np.float64).T
+
+
+def _down_transposed(u, w_up, w_down):
+    h = np.maximum(np.asarray(u, np.float64) @ np.asarray(w_up, np.float64).T, 0.0) ** 2
+    return h @ np.asarray(w_down, np.float64)
+
+
+def _no_renorm(s, idx, rho):
+    sel = np.take_along_axis(np.asarray(s, np.float32), idx, 1)
+    return (sel * np.float32(rho)).astype(np.float32)
+
+
+_orig_renorm = O.renormalize
+
+
+def _no_scale(s, idx, rho):
+    return _orig_renorm(s, idx, 1.0)
+
+
+_orig_select = O.select_experts
+
+
+def _select_unbiased(s, beta, k):
+    return _orig_select(s, np.zeros_like(np.asarray(beta)), k)
+
+
+def _weights_from_biased(s, idx, rho):
+    return _orig_renorm(np.asarray(s) + _BIAS[None, :], idx, rho)
+
+
+_BIAS = None
+
+
+@pytest.mark.parametrize("name,attr,fn", [
+    ("relu not squared", "expert_mlp", _relu_not_squared),
+    ("up weight transposed", "expert_mlp", _up_transposed),
+    ("down weight transposed", "expert_mlp", _down_transposed),
+    ("no renormalisation", "renormalize", _no_renorm),
+    ("no routed scaling", "renormalize", _no_scale),
+    ("bias ignored in selection", "select_experts", _select_unbiased),
+    ("weights from biased score", "renormalize", _weights_from_biased),
+    ("shared expert dropped", "shared_expert", lambda x, a, b: 0.0 * O.expert_mlp(x, a, b)),
+    ("fc2_latent transposed", "latent_up_projection",
+     lambda r, W2: np.asarray(r) @ np.asarray(W2, np.float64)),
+])
+def test_planted_mistakes_fail_worked_example(monkeypatch, name, attr, fn):
+    global _BIAS
+    g, cfg, x, w = micro_case()
+    _BIAS = np.asarray(w.router_bias, np.float32)
+    monkeypatch.setattr(O, attr, fn)
+    # a wrong result or a shape error both count as caught
+    with pytest.raises((AssertionError, ValueError)):
+        check_micro(O.forward(x, w, cfg), g["expected"])
+
+
+def test_bf16_upcast_exact():
+    vals = np.array([0.0, -0.0, 1.0, -2.5, 3.140625, 1e-30, -65280.0, 2.0 ** -133], np.float32)
+    bits = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    back = O.bf16_bits_to_f64(bits)
+    trunc = (vals.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(back, trunc)
+    assert O.bf16_bits_to_f64(np.array([0x3F80], np.uint16))[0] == 1.0
+    assert O.bf16_bits_to_f64(np.array([0xC000], np.uint16))[0] == -2.0
+
+
+def test_sigmoid_closed_forms():
+    ln3 = math.log(3.0)
+    wg = np.array([[0.0], [ln3], [-ln3], [100.0], [-100.0], [2.0], [-2.0]], np.float32)
+    logits, s = O.router_scores(np.ones((1, 1), np.float32), wg)
+    assert logits.dtype == np.float32 and s.dtype == np.float32
+    assert s[0, 0] == np.float32(0.5)
+    np.testing.assert_allclose(s[0, 1], 0.75, rtol=2e-7)
+    np.testing.assert_allclose(s[0, 2], 0.25, rtol=2e-7)
+    assert s[0, 3] == np.float32(1.0)
+    # e^-100 is subnormal in float32: correct to within half a subnormal step
+    assert abs(float(s[0, 4]) - math.exp(-100.0)) <= 0.5 * 2.0 ** -149
+    # symmetry sigma(-l) = 1 - sigma(l), and the textbook value at 2
+    assert abs(float(s[0, 5]) + float(s[0, 6]) - 1.0) < 1e-7
+    np.testing.assert_allclose(s[0, 5], 1.0 / (1.0 + math.exp(-2.0)), rtol=1e-7)
+
+
+def test_gemm_exact_on_integers():
+    rng = np.random.default_rng(5)
+    x = rng.integers(-8, 9, size=(5, 7))
+    W = rng.integers(-8, 9, size=(3, 7))
+    got = O.latent_projection(x, W)
+    for t in range(5):
+        for r in range(3):
+            assert got[t, r] == sum(int(x[t, d]) * int(W[r, d]) for d in range(7))
+    u = rng.integers(-3, 4, size=(4, 6))
+    wu = rng.integers(-3, 4, size=(5, 6))
+    wd = rng.integers(-3, 4, size=(6, 5))
+    got = O.expert_mlp(u, wu, wd)
+    for t in range(4):
+        h = [max(0, sum(int(u[t, j]) * int(wu[f, j]) for j in range(6))) ** 2 for f in range(5)]
+        for o in range(6):
+            assert got[t, o] == sum(h[f] * int(wd[o, f]) for f in range(5))
+
+
+def test_topk_matches_subset_enumeration():
+    rng = np.random.default_rng(1)
+    E, K, T = 16, 4, 40
+    s = rng.uniform(0, 1, size=(T, E)).astype(np.float32)
+    beta = rng.normal(0, 0.1, size=E).astype(np.float32)
+    idx, b, gap = O.select_experts(s, beta, K)
+    for t in range(T):
+        best = max(itertools.combinations(range(E), K),
+                   key=lambda c: sum(float(b[t, e]) for e in c))
+        assert tuple(idx[t]) == best
+        kept = sorted((float(b[t, e]) for e in best))
+        rest = max(float(b[t, e]) for e in range(E) if e not in best)
+        assert gap[t] == pytest.approx(kept[0] - rest, abs=0)
+
+
+def test_topk_tie_break_lower_index():
+    # x = 0 gives sigma(0) = 0.5 for every expert; the bias alone decides.
+    s = np.full((1, 8), 0.5, np.float32)
+    beta = np.array([0.1, 0.3, 0.3, 0.2, 0.3, 0.0, 0.2, 0.3], np.float32)
+    idx, _, gap = O.select_experts(s, beta, 3)
+    assert idx.tolist() == [[1, 2, 4]]
+    assert gap[0] == 0.0
+    idx, _, _ = O.select_experts(s, beta, 5)
+    assert idx.tolist() == [[1, 2, 3, 4, 7]]
+    # -0.0 and +0.0 compare equal: the lower index wins
+    idx, _, _ = O.select_experts(np.zeros((1, 3), np.float32),
+                                 np.array([0.0, -0.0, 0.0], np.float32), 1)
+    assert idx.tolist() == [[0]]
+
+
+def test_renormalisation_invariants():
+    rng = np.random.default_rng(2)
+    E, T = 64, 200
+    s = rng.uniform(0.01, 1.0, size=(T, E)).astype(np.float32)
+    for K in (1, 2, 7, 22):
+        idx = np.sort(rng.permuted(np.tile(np.arange(E), (T, 1)), axis=1)[:, :K], axis=1)
+        w = O.renormalize(s, idx, 5.0)
+        assert w.dtype == np.float32
+        tot = w.astype(np.float64).sum(1)
+        assert np.all(np.abs(tot - 5.0) <= 32 * np.spacing(np.float32(5.0)))
+        if K == 1:
+            assert np.all(w == np.float32(5.0))
+    idx = np.tile(np.arange(E), (T, 1))
+    w = O.renormalize(s, idx, 5.0)
+    ref = 5.0 * s.astype(np.float64) / np.array([math.fsum(r) for r in s.astype(np.float64)])[:, None]
+    np.testing.assert_allclose(w, ref, rtol=3e-6)
+
+
+def tiny_inputs(seed=0, **kw):
+    wl = li.workload("tiny", seed=seed, **kw)
+    inp = li.make_inputs(wl, "cpu")
+    w = li.HostWeights(inp, eager_experts=True)
+    sh = wl.shape
+    cfg = O.OracleConfig(sh.hidden_size, sh.moe_latent_size, sh.n_routed_experts,
+                         sh.num_experts_per_tok, sh.moe_intermediate_size,
+                         sh.moe_shared_expert_intermediate_size, sh.routed_scaling_factor)
+    return li.bf16_bits(inp.x), w, cfg
+
+
+def test_dense_formulation_matches_sparse_dispatch():
+    x, w, cfg = tiny_inputs()
+    out = O.forward(x, w, cfg)
+    z = out["z"]
+    E = cfg.n_routed_experts
+    gate = np.zeros((x.shape[0], E))
+    for t in range(x.shape[0]):
+        for k in range(cfg.num_experts_per_tok):
+            gate[t, out["idx"][t, k]] = out["w"][t, k]
+    r = np.zeros_like(z)
+    for e in range(E):
+        h = np.maximum(z @ O.bf16_bits_to_f64(w.expert_up[e]).T, 0) ** 2
+        r += gate[:, e:e + 1] * (h @ O.bf16_bits_to_f64(w.expert_down[e]).T)
+    np.testing.assert_allclose(out["r"], r, rtol=1e-12, atol=1e-12 * np.abs(r).max())
+    assert out["counts"].sum() == x.shape[0] * cfg.num_experts_per_tok
+
+
+def test_zero_input_gives_zero_output_and_bias_ranking():
+    x, w, cfg = tiny_inputs()
+    x0 = np.zeros_like(x)
+    out = O.forward(x0, w, cfg)
+    assert np.all(out["y"] == 0.0)
+    assert np.all(out["s"] == np.float32(0.5))
+    want = np.sort(np.argsort(-w.router_bias, kind="stable")[:cfg.num_experts_per_tok])
+    assert np.all(out["idx"] == want[None, :])
+
+
+def test_zero_expert_up_gives_shared_only():
+    x, w, cfg = tiny_inputs()
+    w.expert_up = np.zeros_like(w.expert_up)
+    out = O.forward(x, w, cfg)
+    assert np.all(out["y_routed"] == 0.0)
+    np.testing.assert_array_equal(out["y"], out["y_shared"])
+
+
+def test_identical_experts_give_rho_times_one_expert():
+    x, w, cfg = tiny_inputs()
+    w.expert_up = np.broadcast_to(w.expert_up[3], w.expert_up.shape).copy()
+    w.expert_down = np.broadcast_to(w.expert_down[3], w.expert_down.shape).copy()
+    out = O.forward(x, w, cfg)
+    one = O.expert_mlp(out["z"], O.bf16_bits_to_f64(w.expert_up[3]),
+                       O.bf16_bits_to_f64(w.expert_down[3]))
+    np.testing.assert_allclose(out["r"], cfg.routed_scaling_factor * one,
+                               rtol=1e-6, atol=1e-6 * np.abs(one).max())
+
+
+def test_token_order_equivariance():
+    x, w, cfg = tiny_inputs()
+    out = O.forward(x, w, cfg)
+    perm = np.random.default_rng(3).permutation(x.shape[0])
+    outp = O.forward(x[perm], w, cfg)
+    np.testing.assert_array_equal(outp["idx"], out["idx"][perm])
+    np.testing.assert_array_equal(outp["w"], out["w"][perm])
+    np.testing.assert_allclose(outp["y"], out["y"][perm], rtol=1e-12, atol=1e-12)
+
+
+def test_forced_selection_is_used():
+    x, w, cfg = tiny_inputs()
+    out = O.forward(x, w, cfg)
+    forced = np.tile(np.arange(cfg.num_experts_per_tok), (x.shape[0], 1))
+    outf = O.forward(x, w, cfg, forced_idx=forced)
+    assert np.all(outf["idx"] == forced)
+    assert not np.allclose(outf["y"], out["y"])
+
+
+def test_single_expert_and_all_experts():
+    x, w, cfg = tiny_inputs()
+    from dataclasses import replace
+    c1 = replace(cfg, num_experts_per_tok=1)
+    out = O.forward(x, w, c1)
+    assert np.all(out["w"] == np.float32(5.0))
+    cE = replace(cfg, num_experts_per_tok=cfg.n_routed_experts)
+    out = O.forward(x, w, cE)
+    assert np.all(out["idx"] == np.arange(cfg.n_routed_experts)[None, :])
+    assert np.all(np.isinf(out["gap"]))
+
+
+def test_page_parameter_and_flop_accounting():
+    # "Nemotron 3 Ultra 架构深度拆解报告", §2.3.4 / §2.3.8 / §3.1.3: with the
+    # gate on the 8192-d hidden state the page prints 10.94 B parameters per
+    # MoE layer, 667.5 M active per token and about 1.33e9 FLOPs per token.
+    sh = li.FULL
+    D, R, E, K = sh.hidden_size, sh.moe_latent_size, sh.n_routed_experts, sh.num_experts_per_tok
+    F, S = sh.moe_intermediate_size, sh.moe_shared_expert_intermediate_size
+    params = E * D + E + 2 * D * R + E * 2 * F * R + 2 * D * S
+    assert round(params / 1e9, 2) == 10.94
+    # the page rounds one expert to 21 M before multiplying by 22
+    per_expert_m = round(2 * F * R / 1e6)
+    active_page = (E * D + 2 * D * R + 2 * D * S) / 1e6 + K * per_expert_m
+    assert per_expert_m == 21 and round(active_page, 1) == 667.5
+    flops = 2 * (E * D + 2 * D * R + K * 2 * F * R + 2 * D * S)
+    assert round(flops / 1e9, 2) == 1.33
+    # the page's single-expert size and the expert total
+    assert 2 * F * R == 20_971_520 and E * 2 * F * R == 10_737_418_240
+
+
+def test_zipf_bias_recipe_shape():
+    b = li.zipf_bias(li.FULL, 3)
+    assert b.dtype == np.float32 and b.shape == (512,)
+    assert (b == np.float32(-2.0)).sum() == 51
+    live = b[b > -1.5]
+    assert np.all(live <= 0.0) and np.all(live > -1.0)
+
+
+def test_tiny_generator_is_seeded():
+    a = li.make_inputs(li.workload("tiny"), "cpu")
+    b = li.make_inputs(li.workload("tiny"), "cpu")
+    assert torch.equal(a.x, b.x) and torch.equal(a.expert_down, b.expert_down)
+    assert a.x.dtype == torch.bfloat16 and a.router.dtype == torch.float32
+    assert a.expert_up.shape == (16, 128, 64) and a.expert_down.shape == (16, 64, 128)
