@@ -1,0 +1,200 @@
+#!/usr/bin/env python3
+"""Benchmark of the LatentMoE layer forward pass on one MI355X.
+
+One step = one whole forward of the layer (every kernel of the path) over one
+batch of synthetic tokens, weights and inputs resident in HBM.  Prints ONE
+JSON line: tokens/s of the layer, the roofline of its dominant kernel
+(timed live with HIP events on the forward's stream), the layer-level
+roofline fraction, and the CPU oracle timed on a bounded sample of the same
+workload on the host's cores.
+
+Default workload: the full-shape decode batch (T = 32 tokens; hidden 8192,
+latent 2048, 512 experts top-22, expert MLP 2048->5120->2048, shared expert
+8192->10240->8192), bf16 weights and activations, fp32 router.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "LatentMoE layer tokens/s; % HBM roofline (decode) / % bf16 MFMA peak (prefill)"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+HBM_BOUND = {"tiny", "decode", "mtp_verify"}
+
+
+def stage_work(sh, T, U):
+    """Algorithmic bytes and flops of each stage for T tokens touching U
+    distinct experts (weights read once, activations read/written once)."""
+    D, R, E = sh.hidden_size, sh.moe_latent_size, sh.n_routed_experts
+    K, F, S = sh.num_experts_per_tok, sh.moe_intermediate_size, sh.moe_shared_expert_intermediate_size
+    slots = T * K
+    b = {
+        "proj_in": (R + S) * D * 2 + T * D * 2 + T * R * 6 + T * S * 2,
+        "router_logits": E * R * 4 + T * R * 4 + T * E * 4,
+        "router_select": T * E * 4 + E * 4 + slots * 8,
+        "dispatch": slots * 4 * 4 + E * 12,
+        "expert_up": U * F * R * 2 + slots * R * 2 + slots * F * 2,
+        "expert_down": U * R * F * 2 + slots * F * 2 + slots * R * 2,
+        "combine": slots * R * 2 + slots * 8 + T * R * 2,
+        "proj_out": D * (R + S) * 2 + T * (R + S) * 2 + T * D * 2,
+    }
+    f = {
+        "proj_in": 2 * T * D * (R + S),
+        "router_logits": 2 * T * R * E,
+        "router_select": 0, "dispatch": 0,
+        "expert_up": 2 * slots * R * F,
+        "expert_down": 2 * slots * F * R,
+        "combine": 2 * slots * R,
+        "proj_out": 2 * T * D * (R + S),
+    }
+    return b, f
+
+
+def bf16_flops(sh, T):
+    D, R, K, F, S = (sh.hidden_size, sh.moe_latent_size, sh.num_experts_per_tok,
+                     sh.moe_intermediate_size, sh.moe_shared_expert_intermediate_size)
+    return 2 * T * (2 * D * R + 2 * K * R * F + 2 * D * S)
+
+
+def cpu_baseline(inp, sh, n_tokens):
+    """The CPU oracle, as it stands, on the first n_tokens tokens of the batch."""
+    import numpy as np
+    import lmoe_inputs as li
+    from oracle import lmoe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    cfg = O.OracleConfig(sh.hidden_size, sh.moe_latent_size, sh.n_routed_experts,
+                         sh.num_experts_per_tok, sh.moe_intermediate_size,
+                         sh.moe_shared_expert_intermediate_size, sh.routed_scaling_factor)
+    hw = li.HostWeights(inp)                       # dense weights copied to the host
+    x = li.bf16_bits(inp.x[:n_tokens])
+    t0 = time.perf_counter()
+    O.forward(x, hw, cfg)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"first {n_tokens} tokens of the same batch through the float64 NumPy "
+                       f"oracle ({dt:.1f} s; includes upcasting each touched expert and its "
+                       f"device-to-host copy; BLAS threads {threads}, host cpus "
+                       f"{len(os.sched_getaffinity(0))})")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode",
+                    choices=["tiny", "decode", "mtp_verify", "prefill", "skewed"])
+    ap.add_argument("--cpu-sample-tokens", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import lmoe_inputs as li
+    import sparse_moe_layer_latentmoe_amd as pkg
+
+    dev = torch.device("cuda:0")
+    wl = li.workload(args.workload)
+    sh, T = wl.shape, wl.tokens
+    inp = li.make_inputs(wl, dev)
+    weights = {k: getattr(inp, k) for k in (
+        "fc1_latent", "router", "router_bias", "expert_up", "expert_down",
+        "fc2_latent", "shared_up", "shared_down")}
+    layer = pkg.LatentMoE(sh, weights, max_tokens=T)
+    y = torch.empty_like(inp.x)
+    counts = torch.empty(sh.n_routed_experts, dtype=torch.int32, device=dev)
+    layer.forward_into(inp.x, y, pkg.Taps(expert_counts=counts))
+    torch.cuda.synchronize()
+    U = int((counts > 0).sum().item())
+    for _ in range(args.warmup):
+        layer.forward_into(inp.x, y)
+    torch.cuda.synchronize()
+
+    layer.profile_begin(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.forward_into(inp.x, y)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages, nf = layer.profile_end()
+    ms = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {k: v / max(nf, 1) for k, v in stages.items()}
+
+    sb, sf = stage_work(sh, T, U)
+    hbm = args.workload in HBM_BOUND
+    dom = max(stage_ms, key=stage_ms.get)
+    if hbm:
+        ach = sb[dom] / (stage_ms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "algorithmic_bytes_per_launch": sb[dom], "avg_launch_ms": round(stage_ms[dom], 5)}
+        layer_bytes = sum(sb.values())
+        layer_ach = layer_bytes / (ms * 1e-3) / 1e9
+        layer_roof = {"bound": "hbm", "achieved": round(layer_ach, 1), "unit": "GB/s",
+                      "frac": round(layer_ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": layer_bytes}
+    else:
+        ach = sf[dom] / (stage_ms[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": dom, "algorithmic_flops_per_launch": sf[dom],
+                "avg_launch_ms": round(stage_ms[dom], 5)}
+        fl = bf16_flops(sh, T)
+        layer_ach = fl / (ms * 1e-3) / 1e12
+        layer_roof = {"bound": "mfma", "achieved": round(layer_ach, 1), "unit": "TFLOP/s",
+                      "frac": round(layer_ach / BF16_PEAK_TFLOPS, 4), "algorithmic_bf16_flops": fl}
+
+    out = {
+        "metric": METRIC,
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: LatentMoE layer forward, T={T} tokens, "
+                               f"hidden {sh.hidden_size}, latent {sh.moe_latent_size}, "
+                               f"{sh.n_routed_experts} experts top-{sh.num_experts_per_tok}, "
+                               f"expert MLP {sh.moe_intermediate_size}, shared "
+                               f"{sh.moe_shared_expert_intermediate_size}, bf16 weights, "
+                               f"fp32 router",
+                   "tokens": T, "seed": wl.seed, "unique_experts": U,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "layer_roofline": layer_roof,
+        "us_per_layer": round(ms * 1e3, 2),
+        "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+    }
+    if not args.no_cpu_baseline:
+        n = min(args.cpu_sample_tokens, T)
+        out["cpu_baseline"] = cpu_baseline(inp, sh, n)
+    print(json.dumps(out), flush=True)
+    layer.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,143 @@
+/*
+ * lmoe.h -- C ABI of the LatentMoE feed-forward layer (forward pass) on
+ * AMD MI355X (gfx950).
+ *
+ * The layer (page "Nemotron 3 Ultra 架构深度拆解报告", CH5 §5.6 "7 步数据流",
+ * Steps 1-7, router moved onto the latent as the page's summary (CH0) and the
+ * page "NVIDIA Nemotron 3 Super 技术解读" §2.2 describe it):
+ *
+ *   z    = x W1^T                          fc1_latent            [T, R]
+ *   l    = z Wg^T, s = sigmoid(l)          fp32 router           [T, E]
+ *   I    = top-K of (s + bias), single group, ties to the lower expert id
+ *   w    = rho * s[I] / (sum s[I] + 1e-20)  rho = routed_scaling_factor
+ *   r    = sum_k w_k relu(z Wup[I_k]^T)^2 Wdn[I_k]^T            [T, R]
+ *   y    = r W2^T + relu(x Wsu^T)^2 Wsd^T  fc2_latent + shared   [T, D]
+ *
+ * Sizes follow the model's config keys (page "Nemotron-3-Labs-Ultra-Math-SFT"
+ * article, 核心配置速查表): D = hidden_size, R = moe_latent_size,
+ * E = n_routed_experts, K = num_experts_per_tok, F = moe_intermediate_size,
+ * S = moe_shared_expert_intermediate_size.
+ *
+ * Conventions for every entry point:
+ *  - bf16 tensors are passed as uint16_t bit patterns; every matrix is
+ *    row-major and dense, weights stored out x in (a linear layer's layout),
+ *    expert weights as 3-D (expert, out, in) tensors (§5.1 of the page above);
+ *  - all tensor pointers are DEVICE pointers, 16-byte aligned, owned by the
+ *    caller; the library never allocates or frees device memory;
+ *  - `stream` is a hipStream_t (NULL = the null stream); work is enqueued
+ *    asynchronously and nothing synchronises the host;
+ *  - arguments are checked on the host before any HIP call; on error nothing
+ *    is enqueued and the status says why.  Device faults surface at the
+ *    caller's next synchronisation.  Inputs must be finite.
+ *  - one handle owns one workspace: do not use a handle on two streams at
+ *    the same time.
+ */
+#ifndef LMOE_H
+#define LMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LMOE_OK = 0,
+  LMOE_ERR_INVALID_ARG = -1,     /* NULL / misaligned / aliased pointer, bad value */
+  LMOE_ERR_UNSUPPORTED = -2,     /* a configuration this library does not implement */
+  LMOE_ERR_TOO_MANY_TOKENS = -3, /* T > max_tokens of the handle */
+  LMOE_ERR_WORKSPACE = -4,       /* workspace missing or smaller than lmoe_workspace_size */
+  LMOE_ERR_HIP = -5              /* a HIP launch or copy returned an error */
+} lmoe_status;
+
+/* Path selection for the expert and projection GEMMs.  AUTO picks by token
+ * count (weight streaming for small batches, LDS-tiled MFMA otherwise);
+ * the other values force one tiling for every GEMM (used by tests). */
+typedef enum { LMOE_PATH_AUTO = 0, LMOE_PATH_STREAM = 1, LMOE_PATH_TILED = 2 } lmoe_path;
+
+typedef struct {
+  int32_t hidden_size;                         /* D; multiple of 64 */
+  int32_t moe_latent_size;                     /* R; multiple of 64 */
+  int32_t n_routed_experts;                    /* E; 1..1024 */
+  int32_t num_experts_per_tok;                 /* K; 1..min(E, 64) */
+  int32_t moe_intermediate_size;               /* F; multiple of 64 */
+  int32_t moe_shared_expert_intermediate_size; /* S; multiple of 64 */
+  int32_t n_group;                             /* routing groups: must be 1 */
+  int32_t topk_group;                          /* groups kept: must be 1 */
+  float routed_scaling_factor;                 /* rho, finite (5.0 in the model) */
+  int32_t max_tokens;                          /* largest T a forward may use; sizes the workspace */
+  int32_t path;                                /* lmoe_path */
+} lmoe_config;
+
+/* Device pointers; the handle borrows them and they must outlive it. */
+typedef struct {
+  const uint16_t *fc1_latent;  /* bf16 [R, D] */
+  const float *router;         /* fp32 [E, R]  gate weight */
+  const float *router_bias;    /* fp32 [E]     e_score_correction_bias */
+  const uint16_t *expert_up;   /* bf16 [E, F, R] */
+  const uint16_t *expert_down; /* bf16 [E, R, F] */
+  const uint16_t *fc2_latent;  /* bf16 [D, R] */
+  const uint16_t *shared_up;   /* bf16 [S, D] */
+  const uint16_t *shared_down; /* bf16 [D, S] */
+} lmoe_weights;
+
+/* Optional device outputs of intermediate values (tests, monitoring).  Any
+ * field may be NULL.  Shapes for a forward of T tokens: */
+typedef struct {
+  float *z_f32;           /* [T, R] fp32 latent (the router's input) */
+  int32_t *topk_idx;      /* [T, K] selected experts, ascending id per token */
+  float *topk_w;          /* [T, K] routing weights, same order as topk_idx */
+  int32_t *expert_counts; /* [E] tokens routed to each expert */
+  float *r_latent;        /* [T, R] fp32 weighted sum of expert outputs */
+} lmoe_taps;
+
+typedef struct lmoe_handle lmoe_handle;
+
+/* Bytes of device workspace a handle with this configuration needs;
+ * 0 if the configuration is invalid or unsupported. */
+size_t lmoe_workspace_size(const lmoe_config *cfg);
+
+/* Validate `cfg` and `w`, carve `workspace` (device memory of at least
+ * lmoe_workspace_size(cfg) bytes, 256-byte aligned, caller-owned) and
+ * return a host-side handle in *out.  No HIP call is made. */
+lmoe_status lmoe_create(const lmoe_config *cfg, const lmoe_weights *w, void *workspace,
+                        size_t workspace_bytes, lmoe_handle **out);
+
+/* y = LatentMoE(x) for T tokens.  x: bf16 [T, D], y: bf16 [T, D] (must not
+ * overlap x).  T = 0 is a no-op.  `taps` may be NULL.  Page steps 1-7. */
+lmoe_status lmoe_forward(lmoe_handle *h, const uint16_t *x, int32_t T, uint16_t *y,
+                         void *stream, const lmoe_taps *taps);
+
+/* Router only (page steps 1-4 on a given latent): from z_f32 [T, R] fp32
+ * write topk_idx [T, K] (ascending expert id) and topk_w [T, K]. */
+lmoe_status lmoe_route(lmoe_handle *h, const float *z_f32, int32_t T, int32_t *topk_idx,
+                       float *topk_w, void *stream);
+
+/* Free the handle (host memory only).  NULL is a no-op. */
+void lmoe_destroy(lmoe_handle *h);
+
+/* Static text for a status code. */
+const char *lmoe_status_string(lmoe_status s);
+
+/* ---- per-kernel timing (HIP events on the forward's stream) ------------ */
+
+/* Number of timed stages of lmoe_forward and the name of stage i. */
+int32_t lmoe_num_stages(void);
+const char *lmoe_stage_name(int32_t i);
+
+/* Start timing: the next up to `max_forwards` calls of lmoe_forward record
+ * a HIP event before and after each stage (events are created here; a
+ * hipEventCreate failure returns LMOE_ERR_HIP).  max_forwards <= 4096. */
+lmoe_status lmoe_profile_begin(lmoe_handle *h, int32_t max_forwards);
+
+/* Stop timing: wait for the recorded events, write the summed milliseconds
+ * of each stage over the recorded forwards into ms[0..n_stages) and the
+ * number of recorded forwards into *n_forwards; destroy the events. */
+lmoe_status lmoe_profile_end(lmoe_handle *h, float *ms, int32_t n_stages, int32_t *n_forwards);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LMOE_H */

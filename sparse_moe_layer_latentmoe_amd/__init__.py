@@ -1,0 +1,240 @@
+"""LatentMoE feed-forward layer (forward pass) for AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``liblmoe.so`` (declared in
+``include/lmoe.h``).  The binding only marshals arguments: every step of the
+layer runs in the library's HIP kernels.  PyTorch is used to own device
+memory (weights, workspace, inputs, outputs) and to name the HIP stream.
+
+The library must have been built (``python -m
+sparse_moe_layer_latentmoe_amd._build`` or ``__graft_entry__.build()``);
+loading fails loudly if it is missing -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblmoe.so")
+
+LMOE_OK = 0
+LMOE_ERR_INVALID_ARG = -1
+LMOE_ERR_UNSUPPORTED = -2
+LMOE_ERR_TOO_MANY_TOKENS = -3
+LMOE_ERR_WORKSPACE = -4
+LMOE_ERR_HIP = -5
+
+PATH_AUTO, PATH_STREAM, PATH_TILED = 0, 1, 2
+
+EXPORTED = (
+    "lmoe_workspace_size", "lmoe_create", "lmoe_forward", "lmoe_route", "lmoe_destroy",
+    "lmoe_status_string", "lmoe_num_stages", "lmoe_stage_name", "lmoe_profile_begin",
+    "lmoe_profile_end",
+)
+
+
+class LmoeConfig(ctypes.Structure):
+    _fields_ = [
+        ("hidden_size", ctypes.c_int32),
+        ("moe_latent_size", ctypes.c_int32),
+        ("n_routed_experts", ctypes.c_int32),
+        ("num_experts_per_tok", ctypes.c_int32),
+        ("moe_intermediate_size", ctypes.c_int32),
+        ("moe_shared_expert_intermediate_size", ctypes.c_int32),
+        ("n_group", ctypes.c_int32),
+        ("topk_group", ctypes.c_int32),
+        ("routed_scaling_factor", ctypes.c_float),
+        ("max_tokens", ctypes.c_int32),
+        ("path", ctypes.c_int32),
+    ]
+
+
+class LmoeWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "fc1_latent", "router", "router_bias", "expert_up", "expert_down",
+        "fc2_latent", "shared_up", "shared_down")]
+
+
+class LmoeTaps(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "z_f32", "topk_idx", "topk_w", "expert_counts", "r_latent")]
+
+
+class LmoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load liblmoe.so and declare its C signatures (raises if it is absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build the HIP library first "
+            "(python -m sparse_moe_layer_latentmoe_amd._build)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    lib.lmoe_workspace_size.argtypes = [ctypes.POINTER(LmoeConfig)]
+    lib.lmoe_workspace_size.restype = ctypes.c_size_t
+    lib.lmoe_create.argtypes = [ctypes.POINTER(LmoeConfig), ctypes.POINTER(LmoeWeights), P,
+                                ctypes.c_size_t, ctypes.POINTER(P)]
+    lib.lmoe_create.restype = ctypes.c_int
+    lib.lmoe_forward.argtypes = [P, P, ctypes.c_int32, P, P, ctypes.POINTER(LmoeTaps)]
+    lib.lmoe_forward.restype = ctypes.c_int
+    lib.lmoe_route.argtypes = [P, P, ctypes.c_int32, P, P, P]
+    lib.lmoe_route.restype = ctypes.c_int
+    lib.lmoe_destroy.argtypes = [P]
+    lib.lmoe_destroy.restype = None
+    lib.lmoe_status_string.argtypes = [ctypes.c_int]
+    lib.lmoe_status_string.restype = ctypes.c_char_p
+    lib.lmoe_num_stages.argtypes = []
+    lib.lmoe_num_stages.restype = ctypes.c_int32
+    lib.lmoe_stage_name.argtypes = [ctypes.c_int32]
+    lib.lmoe_stage_name.restype = ctypes.c_char_p
+    lib.lmoe_profile_begin.argtypes = [P, ctypes.c_int32]
+    lib.lmoe_profile_begin.restype = ctypes.c_int
+    lib.lmoe_profile_end.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
+                                     ctypes.POINTER(ctypes.c_int32)]
+    lib.lmoe_profile_end.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().lmoe_status_string(status).decode()
+
+
+def stage_names() -> list:
+    lib = load_library()
+    return [lib.lmoe_stage_name(i).decode() for i in range(lib.lmoe_num_stages())]
+
+
+def make_config(shape, max_tokens: int, path: int = PATH_AUTO) -> LmoeConfig:
+    """Config struct from any object with the model's config-key attributes."""
+    return LmoeConfig(
+        shape.hidden_size, shape.moe_latent_size, shape.n_routed_experts,
+        shape.num_experts_per_tok, shape.moe_intermediate_size,
+        shape.moe_shared_expert_intermediate_size, 1, 1,
+        float(shape.routed_scaling_factor), int(max_tokens), int(path))
+
+
+def workspace_size(cfg: LmoeConfig) -> int:
+    return int(load_library().lmoe_workspace_size(ctypes.byref(cfg)))
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream_handle(stream) -> int | None:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    return int(getattr(stream, "cuda_stream", stream))
+
+
+@dataclass
+class Taps:
+    """Optional device outputs (torch tensors) of one forward."""
+    z_f32: object = None
+    topk_idx: object = None
+    topk_w: object = None
+    expert_counts: object = None
+    r_latent: object = None
+
+    def as_struct(self) -> LmoeTaps:
+        return LmoeTaps(_ptr(self.z_f32), _ptr(self.topk_idx), _ptr(self.topk_w),
+                        _ptr(self.expert_counts), _ptr(self.r_latent))
+
+
+class LatentMoE:
+    """One LatentMoE layer bound to caller-owned device weights.
+
+    ``weights`` maps the lmoe_weights field names to contiguous device
+    tensors (bf16, the router and its bias fp32).  The workspace is a
+    uint8 device tensor allocated here with torch; the library itself never
+    allocates."""
+
+    def __init__(self, shape, weights: dict, max_tokens: int, path: int = PATH_AUTO,
+                 device=None):
+        import torch
+        self.lib = load_library()
+        self.shape = shape
+        self.cfg = make_config(shape, max_tokens, path)
+        ws_bytes = workspace_size(self.cfg)
+        if ws_bytes == 0:
+            raise LmoeError(LMOE_ERR_UNSUPPORTED, "lmoe_workspace_size")
+        dev = device if device is not None else weights["fc1_latent"].device
+        self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        self.weights = {k: v.contiguous() for k, v in weights.items()}
+        self.wstruct = LmoeWeights(*[_ptr(self.weights[n]) for n, _ in LmoeWeights._fields_])
+        h = ctypes.c_void_p()
+        st = self.lib.lmoe_create(ctypes.byref(self.cfg), ctypes.byref(self.wstruct),
+                                  _ptr(self.workspace), ws_bytes, ctypes.byref(h))
+        if st != LMOE_OK:
+            raise LmoeError(st, "lmoe_create")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.lmoe_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def forward_into(self, x, y, taps: Taps | None = None, stream=None) -> None:
+        """y <- LatentMoE(x); x, y bf16 [T, D] device tensors."""
+        ts = taps.as_struct() if taps is not None else None
+        st = self.lib.lmoe_forward(self.handle, _ptr(x), int(x.shape[0]), _ptr(y),
+                                   _stream_handle(stream),
+                                   ctypes.byref(ts) if ts is not None else None)
+        if st != LMOE_OK:
+            raise LmoeError(st, "lmoe_forward")
+
+    def forward(self, x, taps: Taps | None = None, stream=None):
+        import torch
+        y = torch.empty_like(x)
+        self.forward_into(x, y, taps, stream)
+        return y
+
+    __call__ = forward
+
+    def route(self, z_f32, stream=None):
+        """(topk_idx int32 [T, K], topk_w fp32 [T, K]) from a given fp32 latent."""
+        import torch
+        T = int(z_f32.shape[0])
+        K = self.shape.num_experts_per_tok
+        idx = torch.empty((T, K), dtype=torch.int32, device=z_f32.device)
+        w = torch.empty((T, K), dtype=torch.float32, device=z_f32.device)
+        st = self.lib.lmoe_route(self.handle, _ptr(z_f32), T, _ptr(idx), _ptr(w),
+                                 _stream_handle(stream))
+        if st != LMOE_OK:
+            raise LmoeError(st, "lmoe_route")
+        return idx, w
+
+    def profile_begin(self, max_forwards: int) -> None:
+        st = self.lib.lmoe_profile_begin(self.handle, int(max_forwards))
+        if st != LMOE_OK:
+            raise LmoeError(st, "lmoe_profile_begin")
+
+    def profile_end(self):
+        """{stage name: summed ms}, number of forwards recorded."""
+        n = self.lib.lmoe_num_stages()
+        ms = (ctypes.c_float * n)()
+        nf = ctypes.c_int32()
+        st = self.lib.lmoe_profile_end(self.handle, ms, n, ctypes.byref(nf))
+        if st != LMOE_OK:
+            raise LmoeError(st, "lmoe_profile_end")
+        return dict(zip(stage_names(), list(ms))), int(nf.value)

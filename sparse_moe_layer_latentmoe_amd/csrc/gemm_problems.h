@@ -1,0 +1,110 @@
+// The four bf16 GEMMs of the LatentMoE layer, described for the two GEMM
+// kernels (weight streaming and LDS-tiled).  Every GEMM computes
+//     C[m][n] = sum_k A[m][k] * B[n][k]
+// with A the activations (row m) and B a weight stored out x in (row n), both
+// contiguous along k, and fp32 accumulation.  A problem says where row m of A
+// and row n of B start, for up to two consecutive k segments (k < K0 and
+// k >= K0), and what the epilogue stores for four consecutive columns.
+#pragma once
+#include "lmoe_device.h"
+
+namespace lmoe {
+
+// [z | Hs] = x [W1 ; Wsu]^T  (fc1_latent and the shared expert's up
+// projection share the input x; page "Nemotron 3 Ultra 架构深度拆解报告",
+// CH5 §5.6 Steps 5 and 7).  Columns n < R give the latent z, stored fp32
+// (router input) and bf16 (expert input); columns n >= R give the shared
+// expert's hidden relu(.)^2 in bf16.
+struct ProjIn {
+  const uint16_t* x;
+  const uint16_t* w1;
+  const uint16_t* wsu;
+  float* z32;
+  uint16_t* z16;
+  uint16_t* hs;
+  int T, D, R, S;
+  __device__ int N() const { return R + S; }
+  __device__ int K() const { return D; }
+  __device__ int K0() const { return D; }
+  __device__ const uint16_t* b_row0(int, int n) const {
+    return n < R ? w1 + (size_t)n * D : wsu + (size_t)(n - R) * D;
+  }
+  __device__ const uint16_t* b_row1(int, int) const { return nullptr; }
+  __device__ const uint16_t* a_row0(int m) const { return x + (size_t)m * D; }
+  __device__ const uint16_t* a_row1(int) const { return nullptr; }
+  __device__ void store(int, int m, int n, f32x4 v) const {
+    if (n < R) {
+      *reinterpret_cast<f32x4*>(z32 + (size_t)m * R + n) = v;
+      store4_bf16(z16 + (size_t)m * R + n, v);
+    } else {
+      store4_bf16_relu_sq(hs + (size_t)m * S + (n - R), v);
+    }
+  }
+};
+
+// y = [r | Hs] [W2 | Wsd]^T  (fc2_latent plus the shared expert's down
+// projection, Step 7: the routed and shared outputs are added, so one GEMM
+// over the concatenated k range gives their sum with a single rounding).
+struct ProjOut {
+  const uint16_t* r16;
+  const uint16_t* hs;
+  const uint16_t* w2;
+  const uint16_t* wsd;
+  uint16_t* y;
+  int T, D, R, S;
+  __device__ int N() const { return D; }
+  __device__ int K() const { return R + S; }
+  __device__ int K0() const { return R; }
+  __device__ const uint16_t* b_row0(int, int n) const { return w2 + (size_t)n * R; }
+  __device__ const uint16_t* b_row1(int, int n) const { return wsd + (size_t)n * S; }
+  __device__ const uint16_t* a_row0(int m) const { return r16 + (size_t)m * R; }
+  __device__ const uint16_t* a_row1(int m) const { return hs + (size_t)m * S; }
+  __device__ void store(int, int m, int n, f32x4 v) const {
+    store4_bf16(y + (size_t)m * D + n, v);
+  }
+};
+
+// Expert up projection + relu^2 (Step 6), grouped by expert: row p of the
+// expert-sorted slot list reads the bf16 latent of token rows_tok[p].
+struct ExpUp {
+  const uint16_t* z16;
+  const int32_t* rows_tok;
+  const uint16_t* wup;  // [E, F, R]
+  uint16_t* h;          // [slots, F]
+  int R, F;
+  __device__ int N() const { return F; }
+  __device__ int K() const { return R; }
+  __device__ int K0() const { return R; }
+  __device__ const uint16_t* b_row0(int e, int n) const {
+    return wup + ((size_t)e * F + n) * R;
+  }
+  __device__ const uint16_t* b_row1(int, int) const { return nullptr; }
+  __device__ const uint16_t* a_row0(int p) const { return z16 + (size_t)rows_tok[p] * R; }
+  __device__ const uint16_t* a_row1(int) const { return nullptr; }
+  __device__ void store(int, int p, int n, f32x4 v) const {
+    store4_bf16_relu_sq(h + (size_t)p * F + n, v);
+  }
+};
+
+// Expert down projection (Step 6): O[p] = H[p] Wdn[e]^T, stored bf16; the
+// routing weight is applied by the combine.
+struct ExpDown {
+  const uint16_t* h;    // [slots, F]
+  const uint16_t* wdn;  // [E, R, F]
+  uint16_t* o;          // [slots, R]
+  int R, F;
+  __device__ int N() const { return R; }
+  __device__ int K() const { return F; }
+  __device__ int K0() const { return F; }
+  __device__ const uint16_t* b_row0(int e, int n) const {
+    return wdn + ((size_t)e * R + n) * F;
+  }
+  __device__ const uint16_t* b_row1(int, int) const { return nullptr; }
+  __device__ const uint16_t* a_row0(int p) const { return h + (size_t)p * F; }
+  __device__ const uint16_t* a_row1(int) const { return nullptr; }
+  __device__ void store(int, int p, int n, f32x4 v) const {
+    store4_bf16(o + (size_t)p * R + n, v);
+  }
+};
+
+}  // namespace lmoe

@@ -1,0 +1,52 @@
+// Host-side launchers of the gfx950 kernels (each defined next to its kernel).
+// All launchers enqueue on `s` and return hipGetLastError() of the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lmoe {
+
+struct ProjIn;
+struct ProjOut;
+struct ExpUp;
+struct ExpDown;
+struct Tile;
+
+// Weight-streaming GEMMs (few tokens; expert tiles of 16 rows).
+hipError_t stream_proj_in(const ProjIn& p, hipStream_t s);
+hipError_t stream_proj_out(const ProjOut& p, hipStream_t s);
+hipError_t stream_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, int max_tiles,
+                         hipStream_t s);
+hipError_t stream_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles, int max_tiles,
+                           hipStream_t s);
+constexpr int kStreamTileM = 16;
+
+// LDS-tiled MFMA GEMMs (many tokens; expert tiles of tiled_block_m() rows;
+// every N must be a multiple of tiled_block_n()).
+hipError_t tiled_proj_in(const ProjIn& p, hipStream_t s);
+hipError_t tiled_proj_out(const ProjOut& p, hipStream_t s);
+hipError_t tiled_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, int max_tiles,
+                        hipStream_t s);
+hipError_t tiled_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles, int max_tiles,
+                          hipStream_t s);
+int tiled_block_m();
+int tiled_block_n();
+
+// Router: fp32 logits [T, E], then per token sigmoid / bias / top-K / weights.
+hipError_t router_logits(const float* z, const float* wg, float* logits, int T, int E, int R,
+                         hipStream_t s);
+hipError_t router_select(const float* logits, const float* bias, int T, int E, int K, float rho,
+                         int32_t* idx, float* w, hipStream_t s);
+
+// Grouping by expert: counts[E], offsets[E+1], rows_tok[T*K], inv[T*K] and
+// the tile list (tiles of at most tile_m rows) with its length in *ntiles.
+// blockcnt is scratch of ceil(T/64) * E ints.
+hipError_t dispatch(const int32_t* idx, int T, int K, int E, int32_t* blockcnt, int32_t* counts,
+                    int32_t* offsets, int32_t* rows_tok, int32_t* inv, Tile* tiles,
+                    int32_t* ntiles, int tile_m, hipStream_t s);
+
+// r = sum_k w[t][k] O[inv[t][k]] -> r16 (bf16) and, if r32 != NULL, fp32.
+hipError_t combine(const uint16_t* o, const int32_t* inv, const float* w, int T, int K, int R,
+                   uint16_t* r16, float* r32, hipStream_t s);
+
+}  // namespace lmoe

@@ -1,0 +1,349 @@
+// C ABI of the LatentMoE layer: argument checks, workspace carving and the
+// launch sequence of one forward pass.  See include/lmoe.h for the contract.
+//
+// Launch sequence (one stream, no host synchronisation; page "Nemotron 3
+// Ultra 架构深度拆解报告", CH5 §5.6 Steps 1-7):
+//   proj_in        x -> z (fp32 + bf16) and the shared expert's relu^2 hidden
+//   router_logits  z (fp32) -> logits                          (Step 1)
+//   router_select  logits -> top-K experts and weights         (Steps 2-4)
+//   dispatch       experts -> expert-sorted rows + tile list   (Step 6 grouping)
+//   expert_up      relu(z16 Wup[e]^T)^2                        (Step 6)
+//   expert_down    H Wdn[e]^T                                  (Step 6)
+//   combine        r = sum_k w O                               (Step 6 index_add_)
+//   proj_out       y = r W2^T + Hs Wsd^T                       (Step 7)
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/lmoe.h"
+#include "gemm_problems.h"
+#include "kernels.h"
+
+using namespace lmoe;
+
+namespace {
+
+constexpr int kNumStages = 8;
+const char* const kStageNames[kNumStages] = {"proj_in",     "router_logits", "router_select",
+                                             "dispatch",    "expert_up",     "expert_down",
+                                             "combine",     "proj_out"};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool tiled_dims_ok(const lmoe_config& c) {
+  const int bn = tiled_block_n();
+  return (c.moe_latent_size + c.moe_shared_expert_intermediate_size) % bn == 0 &&
+         c.hidden_size % bn == 0 && c.moe_intermediate_size % bn == 0 &&
+         c.moe_latent_size % bn == 0;
+}
+
+lmoe_status check_config(const lmoe_config* c) {
+  if (!c) return LMOE_ERR_INVALID_ARG;
+  if (c->hidden_size <= 0 || c->moe_latent_size <= 0 || c->n_routed_experts <= 0 ||
+      c->num_experts_per_tok <= 0 || c->moe_intermediate_size <= 0 ||
+      c->moe_shared_expert_intermediate_size <= 0 || c->max_tokens <= 0 ||
+      !std::isfinite(c->routed_scaling_factor))
+    return LMOE_ERR_INVALID_ARG;
+  if (c->path < LMOE_PATH_AUTO || c->path > LMOE_PATH_TILED) return LMOE_ERR_INVALID_ARG;
+  if (c->n_group != 1 || c->topk_group != 1) return LMOE_ERR_UNSUPPORTED;
+  if (c->hidden_size % 64 || c->moe_latent_size % 64 || c->moe_intermediate_size % 64 ||
+      c->moe_shared_expert_intermediate_size % 64)
+    return LMOE_ERR_UNSUPPORTED;
+  if (c->n_routed_experts > 1024 || c->n_routed_experts % 16) return LMOE_ERR_UNSUPPORTED;
+  if (c->num_experts_per_tok > c->n_routed_experts || c->num_experts_per_tok > 64)
+    return LMOE_ERR_UNSUPPORTED;
+  if (c->max_tokens > (1 << 22)) return LMOE_ERR_UNSUPPORTED;
+  if (c->path == LMOE_PATH_TILED && !tiled_dims_ok(*c)) return LMOE_ERR_UNSUPPORTED;
+  return LMOE_OK;
+}
+
+// Upper bound on the tile count of the expert tile list for T tokens.
+long max_tiles(const lmoe_config& c, long T, int tile_m) {
+  const long slots = T * c.num_experts_per_tok;
+  return std::min<long>(c.n_routed_experts, slots) + slots / tile_m + 1;
+}
+
+struct Layout {
+  size_t z32, z16, hs, logits, idx, tw, counts, offsets, blockcnt, rows_tok, inv, tiles, ntiles,
+      h, o, r16, total;
+};
+
+Layout make_layout(const lmoe_config& c) {
+  const size_t T = c.max_tokens, R = c.moe_latent_size, S = c.moe_shared_expert_intermediate_size;
+  const size_t E = c.n_routed_experts, K = c.num_experts_per_tok, F = c.moe_intermediate_size;
+  const size_t slots = T * K;
+  const size_t ntile = std::max(max_tiles(c, T, kStreamTileM), max_tiles(c, T, tiled_block_m()));
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  L.z32 = take(T * R * 4);
+  L.z16 = take(T * R * 2);
+  L.hs = take(T * S * 2);
+  L.logits = take(T * E * 4);
+  L.idx = take(slots * 4);
+  L.tw = take(slots * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.blockcnt = take(((T + 63) / 64) * E * 4);
+  L.rows_tok = take(slots * 4);
+  L.inv = take(slots * 4);
+  L.tiles = take(ntile * sizeof(Tile));
+  L.ntiles = take(16);
+  L.h = take(slots * F * 2);
+  L.o = take(slots * R * 2);
+  L.r16 = take(T * R * 2);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+struct lmoe_handle {
+  lmoe_config cfg;
+  lmoe_weights w;
+  char* ws;
+  Layout L;
+  // profiling
+  int prof_max = 0, prof_n = 0;
+  std::vector<hipEvent_t> events;
+
+  template <class T>
+  T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
+};
+
+extern "C" {
+
+size_t lmoe_workspace_size(const lmoe_config* cfg) {
+  if (check_config(cfg) != LMOE_OK) return 0;
+  return make_layout(*cfg).total;
+}
+
+lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, void* workspace,
+                        size_t workspace_bytes, lmoe_handle** out) {
+  if (!out) return LMOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  const lmoe_status st = check_config(cfg);
+  if (st != LMOE_OK) return st;
+  if (!w || !w->fc1_latent || !w->router || !w->router_bias || !w->expert_up ||
+      !w->expert_down || !w->fc2_latent || !w->shared_up || !w->shared_down)
+    return LMOE_ERR_INVALID_ARG;
+  const void* ptrs[8] = {w->fc1_latent, w->router,     w->router_bias, w->expert_up,
+                         w->expert_down, w->fc2_latent, w->shared_up,  w->shared_down};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return LMOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(*cfg);
+  if (!workspace || workspace_bytes < L.total) return LMOE_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return LMOE_ERR_WORKSPACE;
+  lmoe_handle* h = new (std::nothrow) lmoe_handle();
+  if (!h) return LMOE_ERR_INVALID_ARG;
+  h->cfg = *cfg;
+  h->w = *w;
+  h->ws = static_cast<char*>(workspace);
+  h->L = L;
+  *out = h;
+  return LMOE_OK;
+}
+
+void lmoe_destroy(lmoe_handle* h) {
+  if (!h) return;
+  for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
+  delete h;
+}
+
+const char* lmoe_status_string(lmoe_status s) {
+  switch (s) {
+    case LMOE_OK: return "ok";
+    case LMOE_ERR_INVALID_ARG: return "invalid argument";
+    case LMOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LMOE_ERR_TOO_MANY_TOKENS: return "token count exceeds max_tokens";
+    case LMOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case LMOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t lmoe_num_stages(void) { return kNumStages; }
+
+const char* lmoe_stage_name(int32_t i) {
+  return (i >= 0 && i < kNumStages) ? kStageNames[i] : nullptr;
+}
+
+lmoe_status lmoe_profile_begin(lmoe_handle* h, int32_t max_forwards) {
+  if (!h || max_forwards <= 0 || max_forwards > 4096) return LMOE_ERR_INVALID_ARG;
+  for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
+  h->events.assign(static_cast<size_t>(max_forwards) * (kNumStages + 1), nullptr);
+  for (auto& e : h->events)
+    if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      return LMOE_ERR_HIP;
+    }
+  h->prof_max = max_forwards;
+  h->prof_n = 0;
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_profile_end(lmoe_handle* h, float* ms, int32_t n_stages, int32_t* n_forwards) {
+  if (!h || !ms || n_stages < kNumStages || !n_forwards) return LMOE_ERR_INVALID_ARG;
+  for (int i = 0; i < kNumStages; ++i) ms[i] = 0.f;
+  lmoe_status st = LMOE_OK;
+  for (int f = 0; f < h->prof_n && st == LMOE_OK; ++f) {
+    hipEvent_t* ev = &h->events[static_cast<size_t>(f) * (kNumStages + 1)];
+    if (hipEventSynchronize(ev[kNumStages]) != hipSuccess) {
+      st = LMOE_ERR_HIP;
+      break;
+    }
+    for (int i = 0; i < kNumStages; ++i) {
+      float t = 0.f;
+      if (hipEventElapsedTime(&t, ev[i], ev[i + 1]) != hipSuccess) {
+        st = LMOE_ERR_HIP;
+        break;
+      }
+      ms[i] += t;
+    }
+  }
+  *n_forwards = h->prof_n;
+  for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
+  h->events.clear();
+  h->prof_max = h->prof_n = 0;
+  return st;
+}
+
+lmoe_status lmoe_route(lmoe_handle* h, const float* z_f32, int32_t T, int32_t* topk_idx,
+                       float* topk_w, void* stream) {
+  if (!h) return LMOE_ERR_INVALID_ARG;
+  if (T < 0) return LMOE_ERR_INVALID_ARG;
+  if (T > h->cfg.max_tokens) return LMOE_ERR_TOO_MANY_TOKENS;
+  if (T == 0) return LMOE_OK;
+  if (!z_f32 || !topk_idx || !topk_w || !aligned16(z_f32) || !aligned16(topk_idx) ||
+      !aligned16(topk_w))
+    return LMOE_ERR_INVALID_ARG;
+  const lmoe_config& c = h->cfg;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* logits = h->at<float>(h->L.logits);
+  if (router_logits(z_f32, h->w.router, logits, T, c.n_routed_experts, c.moe_latent_size, s) !=
+      hipSuccess)
+    return LMOE_ERR_HIP;
+  if (router_select(logits, h->w.router_bias, T, c.n_routed_experts, c.num_experts_per_tok,
+                    c.routed_scaling_factor, topk_idx, topk_w, s) != hipSuccess)
+    return LMOE_ERR_HIP;
+  return LMOE_OK;
+}
+
+lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t* y, void* stream,
+                         const lmoe_taps* taps) {
+  if (!h) return LMOE_ERR_INVALID_ARG;
+  if (T < 0) return LMOE_ERR_INVALID_ARG;
+  if (T > h->cfg.max_tokens) return LMOE_ERR_TOO_MANY_TOKENS;
+  if (T == 0) return LMOE_OK;
+  const lmoe_config& c = h->cfg;
+  const int D = c.hidden_size, R = c.moe_latent_size, E = c.n_routed_experts;
+  const int K = c.num_experts_per_tok, F = c.moe_intermediate_size;
+  const int S = c.moe_shared_expert_intermediate_size;
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return LMOE_ERR_INVALID_ARG;
+  const size_t xb = static_cast<size_t>(T) * D * 2;
+  const char* xc = reinterpret_cast<const char*>(x);
+  const char* yc = reinterpret_cast<const char*>(y);
+  if (xc < yc + xb && yc < xc + xb) return LMOE_ERR_INVALID_ARG;
+  if (taps) {
+    const void* tp[5] = {taps->z_f32, taps->topk_idx, taps->topk_w, taps->expert_counts,
+                         taps->r_latent};
+    for (const void* p : tp)
+      if (p && !aligned16(p)) return LMOE_ERR_INVALID_ARG;
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool tiled_ok = tiled_dims_ok(c);
+  const bool dense_tiled =
+      tiled_ok && (c.path == LMOE_PATH_TILED || (c.path == LMOE_PATH_AUTO && T > 64));
+  const bool expert_tiled =
+      tiled_ok && (c.path == LMOE_PATH_TILED ||
+                   (c.path == LMOE_PATH_AUTO && static_cast<long>(T) * K > 32L * E));
+  const int tile_m = expert_tiled ? tiled_block_m() : kStreamTileM;
+  const int ntile_max = static_cast<int>(max_tiles(c, T, tile_m));
+
+  float* z32 = h->at<float>(h->L.z32);
+  uint16_t* z16 = h->at<uint16_t>(h->L.z16);
+  uint16_t* hs = h->at<uint16_t>(h->L.hs);
+  float* logits = h->at<float>(h->L.logits);
+  int32_t* idx = h->at<int32_t>(h->L.idx);
+  float* tw = h->at<float>(h->L.tw);
+  int32_t* counts = h->at<int32_t>(h->L.counts);
+  int32_t* offsets = h->at<int32_t>(h->L.offsets);
+  int32_t* blockcnt = h->at<int32_t>(h->L.blockcnt);
+  int32_t* rows_tok = h->at<int32_t>(h->L.rows_tok);
+  int32_t* inv = h->at<int32_t>(h->L.inv);
+  Tile* tiles = h->at<Tile>(h->L.tiles);
+  int32_t* ntiles = h->at<int32_t>(h->L.ntiles);
+  uint16_t* H = h->at<uint16_t>(h->L.h);
+  uint16_t* O = h->at<uint16_t>(h->L.o);
+  uint16_t* r16 = h->at<uint16_t>(h->L.r16);
+
+  hipEvent_t* ev = nullptr;
+  if (h->prof_n < h->prof_max)
+    ev = &h->events[static_cast<size_t>(h->prof_n++) * (kNumStages + 1)];
+  int stage = 0;
+  auto mark = [&]() -> bool {
+    if (!ev) return true;
+    return hipEventRecord(ev[stage++], s) == hipSuccess;
+  };
+  auto ok = [](hipError_t e) { return e == hipSuccess; };
+
+  if (!mark()) return LMOE_ERR_HIP;
+  ProjIn pin{x, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S};
+  if (!ok(dense_tiled ? tiled_proj_in(pin, s) : stream_proj_in(pin, s))) return LMOE_ERR_HIP;
+  if (!mark()) return LMOE_ERR_HIP;
+  if (!ok(router_logits(z32, h->w.router, logits, T, E, R, s))) return LMOE_ERR_HIP;
+  if (!mark()) return LMOE_ERR_HIP;
+  if (!ok(router_select(logits, h->w.router_bias, T, E, K, c.routed_scaling_factor, idx, tw, s)))
+    return LMOE_ERR_HIP;
+  if (!mark()) return LMOE_ERR_HIP;
+  if (!ok(dispatch(idx, T, K, E, blockcnt, counts, offsets, rows_tok, inv, tiles, ntiles, tile_m,
+                   s)))
+    return LMOE_ERR_HIP;
+  if (!mark()) return LMOE_ERR_HIP;
+  ExpUp pup{z16, rows_tok, h->w.expert_up, H, R, F};
+  if (!ok(expert_tiled ? tiled_exp_up(pup, tiles, ntiles, ntile_max, s)
+                       : stream_exp_up(pup, tiles, ntiles, ntile_max, s)))
+    return LMOE_ERR_HIP;
+  if (!mark()) return LMOE_ERR_HIP;
+  ExpDown pdn{H, h->w.expert_down, O, R, F};
+  if (!ok(expert_tiled ? tiled_exp_down(pdn, tiles, ntiles, ntile_max, s)
+                       : stream_exp_down(pdn, tiles, ntiles, ntile_max, s)))
+    return LMOE_ERR_HIP;
+  if (!mark()) return LMOE_ERR_HIP;
+  if (!ok(combine(O, inv, tw, T, K, R, r16, taps ? taps->r_latent : nullptr, s)))
+    return LMOE_ERR_HIP;
+  if (!mark()) return LMOE_ERR_HIP;
+  ProjOut pout{r16, hs, h->w.fc2_latent, h->w.shared_down, y, T, D, R, S};
+  if (!ok(dense_tiled ? tiled_proj_out(pout, s) : stream_proj_out(pout, s))) return LMOE_ERR_HIP;
+  if (!mark()) return LMOE_ERR_HIP;
+
+  if (taps) {
+    if (taps->z_f32 &&
+        !ok(hipMemcpyAsync(taps->z_f32, z32, sizeof(float) * T * R, hipMemcpyDeviceToDevice, s)))
+      return LMOE_ERR_HIP;
+    if (taps->topk_idx && !ok(hipMemcpyAsync(taps->topk_idx, idx, sizeof(int32_t) * T * K,
+                                             hipMemcpyDeviceToDevice, s)))
+      return LMOE_ERR_HIP;
+    if (taps->topk_w &&
+        !ok(hipMemcpyAsync(taps->topk_w, tw, sizeof(float) * T * K, hipMemcpyDeviceToDevice, s)))
+      return LMOE_ERR_HIP;
+    if (taps->expert_counts && !ok(hipMemcpyAsync(taps->expert_counts, counts,
+                                                  sizeof(int32_t) * E, hipMemcpyDeviceToDevice, s)))
+      return LMOE_ERR_HIP;
+  }
+  return LMOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,228 @@
+// Router of the LatentMoE layer: fp32 logits of the latent against the gate,
+// sigmoid, correction bias, top-K and renormalisation.
+//
+// Page "Nemotron 3 Ultra 架构深度拆解报告", CH5 §5.6 Steps 1-4: the gate is
+// an fp32 linear layer, scores are sigmoid(logit), the selection uses
+// score + e_score_correction_bias, the weights use the unbiased scores of
+// the selected experts, divided by (their sum + 1e-20) and multiplied by
+// routed_scaling_factor.  One routing group (n_group = 1, §5.5).  This
+// implementation reads the fp32 latent (the router is on the latent).
+//
+// Two kernels: the logits GEMM (fp32 MFMA, weight-streaming layout like the
+// bf16 streaming GEMM) and one wavefront per token for everything after it.
+#include "kernels.h"
+#include "lmoe_device.h"
+
+namespace lmoe {
+
+// logits[t][e] = sum_k z[t][k] * Wg[e][k].  Work-group: 16 experts x MT*16
+// tokens, the k range split over NW waves, partial sums added in LDS in a
+// fixed order.  Each lane loads 4 consecutive floats of its row per 16-wide
+// k step and feeds them to 4 MFMAs (16x16x4): MFMA j takes component j, so
+// lane group q = l/16 covers k = 4q + j -- the same for both operands.
+template <int NW, int MT>
+__global__ __launch_bounds__(NW * 64) void router_logits_kernel(const float* __restrict__ z,
+                                                                const float* __restrict__ wg,
+                                                                float* __restrict__ logits, int T,
+                                                                int E, int R) {
+  __shared__ f32x4 red[NW > 1 ? NW : 1][MT][64];
+  const int eblocks = E / 16;
+  const int eb = blockIdx.x % eblocks;
+  const int m0 = (blockIdx.x / eblocks) * (16 * MT);
+  const int e0 = eb * 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r16 = lane & 15, kq = (lane >> 4) * 4;
+  const int kw = R / NW, kbeg = w * kw;
+  constexpr int KS = 64;  // k per pipeline stage (4 loads of 16 k)
+  const int nit = kw / KS;
+
+  const float* brow = wg + (size_t)(e0 + r16) * R + kbeg + kq;
+  const float* arow[MT];
+  bool av[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int m = m0 + t * 16 + r16;
+    av[t] = m < T;
+    arow[t] = av[t] ? z + (size_t)m * R + kbeg + kq : nullptr;
+  }
+  f32x4 acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  f32x4 wA[4], xA[4][MT], wB[4], xB[4][MT];
+  auto load = [&](f32x4(&wf)[4], f32x4(&xf)[4][MT], int it) {
+    const int k = it * KS;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      wf[u] = *reinterpret_cast<const f32x4*>(brow + k + u * 16);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        xf[u][t] = av[t] ? *reinterpret_cast<const f32x4*>(arow[t] + k + u * 16)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto compute = [&](const f32x4(&wf)[4], const f32x4(&xf)[4][MT]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[t] = mfma_f32(wf[u][j], xf[u][t][j], acc[t]);
+  };
+  if (nit > 0) load(wA, xA, 0);
+  for (int it = 0; it < nit; it += 2) {
+    if (it + 1 < nit) load(wB, xB, it + 1);
+    compute(wA, xA);
+    if (it + 1 < nit) {
+      if (it + 2 < nit) load(wA, xA, it + 2);
+      compute(wB, xB);
+    }
+  }
+  const int ecol = e0 + (lane >> 4) * 4;
+  if constexpr (NW == 1) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+      if (av[t]) *reinterpret_cast<f32x4*>(logits + (size_t)(m0 + t * 16 + r16) * E + ecol) = acc[t];
+  } else {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[w][t][lane] = acc[t];
+    __syncthreads();
+    for (int t = w; t < MT; t += NW) {
+      f32x4 s = red[0][t][lane];
+#pragma unroll
+      for (int v = 1; v < NW; ++v) s += red[v][t][lane];
+      const int m = m0 + t * 16 + r16;
+      if (m < T) *reinterpret_cast<f32x4*>(logits + (size_t)m * E + ecol) = s;
+    }
+  }
+}
+
+// Order-preserving map of a finite float onto uint32 (larger float ->
+// larger integer); -0 is first turned into +0 so the two compare equal.
+__device__ __forceinline__ uint32_t ordered_bits(float b) {
+  if (b == 0.0f) b = 0.0f;
+  const uint32_t u = __float_as_uint(b);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint64_t o = __shfl_xor(v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// One wavefront per token.  Expert e = 64 j + lane lives in slot j of lane
+// `lane`.  Key = (ordered biased score, ~expert id): the largest key is the
+// highest biased score, equal scores going to the lower expert id.  K rounds
+// of a wave-wide maximum pick the K experts; their output order is
+// ascending expert id, the renormalising sum is a plain float32 sum in that
+// order, then w = (s / (sum + 1e-20)) * rho.
+template <int NJ>
+__global__ __launch_bounds__(256) void router_select_kernel(const float* __restrict__ logits,
+                                                           const float* __restrict__ bias, int T,
+                                                           int E, int K, float rho,
+                                                           int32_t* __restrict__ idx_out,
+                                                           float* __restrict__ w_out) {
+  __shared__ float ssel[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= T) return;
+  float s[NJ];
+  uint64_t key[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = j * 64 + lane;
+    if (e < E) {
+      const float l = logits[(size_t)t * E + e];
+      s[j] = 1.0f / (1.0f + expf(-l));
+      const float b = s[j] + bias[e];
+      key[j] = (static_cast<uint64_t>(ordered_bits(b)) << 32) | (0xFFFFFFFFu - (uint32_t)e);
+    } else {
+      s[j] = 0.f;
+      key[j] = 0;
+    }
+  }
+  uint32_t sel = 0;
+  for (int r = 0; r < K; ++r) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (!((sel >> j) & 1u) && key[j] > best) best = key[j];
+    const uint64_t wbest = wave_max_u64(best);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (key[j] == wbest) sel |= 1u << j;
+  }
+  // Position of each selected expert in ascending id order.
+  int base = 0;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const bool on = (sel >> j) & 1u;
+    const uint64_t m = __ballot(on);
+    if (on) {
+      const int pos = base + __popcll(m & below);
+      idx_out[(size_t)t * K + pos] = j * 64 + lane;
+      ssel[wv][pos] = s[j];
+    }
+    base += __popcll(m);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float denom = 0.f;
+  if (lane == 0) {
+    float acc = 0.f;
+    for (int k = 0; k < K; ++k) acc = acc + ssel[wv][k];
+    denom = acc + 1e-20f;
+  }
+  denom = __shfl(denom, 0, 64);
+  if (lane < K) w_out[(size_t)t * K + lane] = (ssel[wv][lane] / denom) * rho;
+}
+
+hipError_t router_logits(const float* z, const float* wg, float* logits, int T, int E, int R,
+                         hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int mt = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
+  const long grid = (long)((T + 16 * mt - 1) / (16 * mt)) * (E / 16);
+  int nw = 1;
+  const int opts[4] = {1, 2, 4, 8};
+  for (int i = 0; i < 4; ++i) {
+    if (R % (opts[i] * 64) != 0) continue;
+    nw = opts[i];
+    if (grid * nw >= 2048) break;
+  }
+#define LMOE_RL(NW_, MT_) \
+  router_logits_kernel<NW_, MT_><<<grid, NW_ * 64, 0, s>>>(z, wg, logits, T, E, R)
+#define LMOE_RL_MT(NW_) \
+  do { if (mt == 1) LMOE_RL(NW_, 1); else if (mt == 2) LMOE_RL(NW_, 2); else LMOE_RL(NW_, 4); } while (0)
+  switch (nw) {
+    case 1: LMOE_RL_MT(1); break;
+    case 2: LMOE_RL_MT(2); break;
+    case 4: LMOE_RL_MT(4); break;
+    default: LMOE_RL_MT(8); break;
+  }
+#undef LMOE_RL_MT
+#undef LMOE_RL
+  return hipGetLastError();
+}
+
+hipError_t router_select(const float* logits, const float* bias, int T, int E, int K, float rho,
+                         int32_t* idx, float* w, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int grid = (T + 3) / 4;
+  const int nj = (E + 63) / 64;
+#define LMOE_RS(NJ_) router_select_kernel<NJ_><<<grid, 256, 0, s>>>(logits, bias, T, E, K, rho, idx, w)
+  if (nj <= 1) LMOE_RS(1);
+  else if (nj <= 2) LMOE_RS(2);
+  else if (nj <= 4) LMOE_RS(4);
+  else if (nj <= 8) LMOE_RS(8);
+  else LMOE_RS(16);
+#undef LMOE_RS
+  return hipGetLastError();
+}
+
+}  // namespace lmoe

@@ -1,0 +1,134 @@
+"""Helpers of the GPU parity tests: run the HIP layer through the C ABI and
+compare it with the CPU oracle on the same seeded inputs.
+
+Bar (stated once here, used by every test):
+* expert selections equal the oracle's exactly, except tokens whose oracle
+  gap between the K-th and (K+1)-th biased score is below TIE_GAP (those are
+  counted, and the oracle is re-run with the GPU's selection for them);
+* the bf16 output is within OUT_REL of the oracle in normwise max relative
+  error, max|y - y_ref| / max|y_ref|.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import numpy as np
+import torch
+
+import lmoe_inputs as li
+import sparse_moe_layer_latentmoe_amd as pkg
+from oracle import lmoe_oracle as O
+
+TIE_GAP = 1e-6
+OUT_REL = 2e-2
+WEIGHT_FIELDS = ("fc1_latent", "router", "router_bias", "expert_up", "expert_down",
+                 "fc2_latent", "shared_up", "shared_down")
+
+
+def oracle_config(sh) -> O.OracleConfig:
+    return O.OracleConfig(sh.hidden_size, sh.moe_latent_size, sh.n_routed_experts,
+                          sh.num_experts_per_tok, sh.moe_intermediate_size,
+                          sh.moe_shared_expert_intermediate_size, sh.routed_scaling_factor)
+
+
+def weight_dict(inp) -> dict:
+    return {k: getattr(inp, k) for k in WEIGHT_FIELDS}
+
+
+@dataclass
+class GpuRun:
+    y: torch.Tensor
+    z32: np.ndarray
+    idx: np.ndarray
+    w: np.ndarray
+    counts: np.ndarray
+    r: np.ndarray
+
+
+def run_gpu(layer: pkg.LatentMoE, x: torch.Tensor) -> GpuRun:
+    T = x.shape[0]
+    sh = layer.shape
+    dev = x.device
+    taps = pkg.Taps(
+        z_f32=torch.empty((T, sh.moe_latent_size), dtype=torch.float32, device=dev),
+        topk_idx=torch.empty((T, sh.num_experts_per_tok), dtype=torch.int32, device=dev),
+        topk_w=torch.empty((T, sh.num_experts_per_tok), dtype=torch.float32, device=dev),
+        expert_counts=torch.empty((sh.n_routed_experts,), dtype=torch.int32, device=dev),
+        r_latent=torch.empty((T, sh.moe_latent_size), dtype=torch.float32, device=dev),
+    )
+    y = layer.forward(x, taps)
+    torch.cuda.synchronize()
+    return GpuRun(y, taps.z_f32.cpu().numpy(), taps.topk_idx.cpu().numpy().astype(np.int64),
+                  taps.topk_w.cpu().numpy(), taps.expert_counts.cpu().numpy(),
+                  taps.r_latent.cpu().numpy())
+
+
+def normwise_rel(got, ref) -> float:
+    ref = np.asarray(ref, np.float64)
+    scale = np.abs(ref).max()
+    return float(np.abs(np.asarray(got, np.float64) - ref).max() / max(scale, 1e-300))
+
+
+@dataclass
+class Report:
+    ties: int
+    mismatched: int
+    rel_y: float
+    rel_r: float
+    rel_z: float
+    max_w_err: float
+
+
+def compare(g: GpuRun, x_bits: np.ndarray, hw, sh, rows=None) -> Report:
+    """Oracle on the rows ``rows`` of the batch (all if None) vs the GPU run."""
+    cfg = oracle_config(sh)
+    sel = np.arange(x_bits.shape[0]) if rows is None else np.asarray(rows)
+    ref = O.forward(x_bits[sel], hw, cfg)
+    tie = ref["gap"] < TIE_GAP
+    gidx = g.idx[sel]
+    mism = int((~np.all(gidx == ref["idx"], axis=1) & ~tie).sum())
+    forced = O.forward(x_bits[sel], hw, cfg, forced_idx=gidx) if (tie.any() or mism) else ref
+    y = g.y.float().cpu().numpy()[sel]
+    return Report(
+        ties=int(tie.sum()), mismatched=mism,
+        rel_y=normwise_rel(y, forced["y"]),
+        rel_r=normwise_rel(g.r[sel], forced["r"]),
+        rel_z=normwise_rel(g.z32[sel], ref["z32"]),
+        max_w_err=float(np.abs(g.w[sel].astype(np.float64) - forced["w"]).max()),
+    )
+
+
+def check_properties(g: GpuRun, sh, T: int) -> None:
+    """Properties that hold at any size (checked on every token)."""
+    K, E = sh.num_experts_per_tok, sh.n_routed_experts
+    assert g.idx.shape == (T, K)
+    assert np.all((g.idx >= 0) & (g.idx < E))
+    assert np.all(np.diff(g.idx, axis=1) > 0), "selections not strictly ascending"
+    assert g.counts.sum() == T * K
+    assert np.array_equal(np.bincount(g.idx.ravel(), minlength=E), g.counts)
+    wsum = g.w.astype(np.float64).sum(1)
+    assert np.all(np.abs(wsum - sh.routed_scaling_factor) <= 1e-5 * sh.routed_scaling_factor)
+    assert np.all(g.w > 0)
+    assert torch.isfinite(g.y.float()).all()
+
+
+def assert_parity(rep: Report, max_ties=None) -> None:
+    assert rep.mismatched == 0, f"{rep.mismatched} non-tie tokens routed differently"
+    if max_ties is not None:
+        assert rep.ties <= max_ties
+    assert rep.rel_z <= 1e-5, rep
+    assert rep.max_w_err <= 5e-5, rep
+    assert rep.rel_r <= OUT_REL, rep
+    assert rep.rel_y <= OUT_REL, rep
+
+
+MEDIUM = li.LayerShape(1024, 256, 32, 6, 512, 1024, 5.0)
+
+
+def medium(tokens=300, **kw):
+    return li.Workload("medium", MEDIUM, tokens, **kw)
+
+
+def with_shape(wl, **shape_kw):
+    return replace(wl, shape=replace(wl.shape, **shape_kw))

@@ -1,0 +1,163 @@
+"""The C ABI on the host: the library loads, exports every symbol the header
+declares, and rejects bad arguments before any HIP call (so these run
+without a GPU)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import lmoe_inputs as li
+import sparse_moe_layer_latentmoe_amd as pkg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lmoe.h")
+
+FAKE = 0x10000  # 256-byte aligned host-side stand-in; never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pkg.LIB_PATH):
+        pytest.fail("liblmoe.so not built (run __graft_entry__.build())")
+    return pkg.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lmoe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for n in ("lmoe_workspace_size", "lmoe_create", "lmoe_forward", "lmoe_route",
+              "lmoe_destroy", "lmoe_status_string"):
+        assert n in names
+    assert set(names) == set(pkg.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", pkg.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(lmoe_\w+)", out))
+    for n in header_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def cfg(**kw):
+    c = pkg.make_config(li.TINY, 64)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def weights(**kw):
+    w = pkg.LmoeWeights(*([FAKE] * 8))
+    for k, v in kw.items():
+        setattr(w, k, v)
+    return w
+
+
+def create(lib, c, w=None, ws=FAKE, nbytes=None):
+    h = ctypes.c_void_p()
+    if nbytes is None:
+        nbytes = lib.lmoe_workspace_size(ctypes.byref(c)) or 1
+    st = lib.lmoe_create(ctypes.byref(c), ctypes.byref(w or weights()), ws, nbytes,
+                         ctypes.byref(h))
+    return st, h
+
+
+def test_workspace_size_and_config_checks(lib):
+    assert lib.lmoe_workspace_size(ctypes.byref(cfg())) > 0
+    full = pkg.make_config(li.FULL, 8192)
+    # at least the expert hidden and output buffers
+    assert lib.lmoe_workspace_size(ctypes.byref(full)) > 8192 * 22 * (5120 + 2048) * 2
+    assert lib.lmoe_workspace_size(None) == 0
+    for bad, status in [
+        (dict(hidden_size=0), pkg.LMOE_ERR_INVALID_ARG),
+        (dict(max_tokens=0), pkg.LMOE_ERR_INVALID_ARG),
+        (dict(routed_scaling_factor=float("inf")), pkg.LMOE_ERR_INVALID_ARG),
+        (dict(path=7), pkg.LMOE_ERR_INVALID_ARG),
+        (dict(n_group=2), pkg.LMOE_ERR_UNSUPPORTED),
+        (dict(topk_group=2), pkg.LMOE_ERR_UNSUPPORTED),
+        (dict(hidden_size=200), pkg.LMOE_ERR_UNSUPPORTED),
+        (dict(moe_intermediate_size=96), pkg.LMOE_ERR_UNSUPPORTED),
+        (dict(n_routed_experts=2048), pkg.LMOE_ERR_UNSUPPORTED),
+        (dict(n_routed_experts=24), pkg.LMOE_ERR_UNSUPPORTED),
+        (dict(num_experts_per_tok=17), pkg.LMOE_ERR_UNSUPPORTED),
+        (dict(num_experts_per_tok=0), pkg.LMOE_ERR_INVALID_ARG),
+        (dict(path=pkg.PATH_TILED), pkg.LMOE_ERR_UNSUPPORTED),  # tiny R=64 < tile
+    ]:
+        c = cfg(**bad)
+        assert lib.lmoe_workspace_size(ctypes.byref(c)) == 0, bad
+        st, h = create(lib, c, nbytes=1 << 30)
+        assert st == status, (bad, st)
+        assert not h.value
+
+
+def test_create_argument_errors(lib):
+    c = cfg()
+    need = lib.lmoe_workspace_size(ctypes.byref(c))
+    assert create(lib, c, weights(expert_up=None))[0] == pkg.LMOE_ERR_INVALID_ARG
+    assert create(lib, c, weights(router=FAKE + 4))[0] == pkg.LMOE_ERR_INVALID_ARG
+    assert create(lib, c, ws=None)[0] == pkg.LMOE_ERR_WORKSPACE
+    assert create(lib, c, nbytes=need - 1)[0] == pkg.LMOE_ERR_WORKSPACE
+    assert create(lib, c, ws=FAKE + 16)[0] == pkg.LMOE_ERR_WORKSPACE
+    assert lib.lmoe_create(ctypes.byref(c), ctypes.byref(weights()), FAKE, need,
+                           None) == pkg.LMOE_ERR_INVALID_ARG
+    st, h = create(lib, c)
+    assert st == pkg.LMOE_OK and h.value
+    lib.lmoe_destroy(h)
+    lib.lmoe_destroy(None)
+
+
+def test_forward_and_route_argument_errors(lib):
+    c = cfg()
+    st, h = create(lib, c)
+    assert st == pkg.LMOE_OK
+    D = c.hidden_size
+    x, y = FAKE, FAKE + 64 * D * 2 + 4096
+    f = lib.lmoe_forward
+    assert f(None, x, 4, y, None, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert f(h, x, -1, y, None, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert f(h, x, 65, y, None, None) == pkg.LMOE_ERR_TOO_MANY_TOKENS
+    assert f(h, x, 0, y, None, None) == pkg.LMOE_OK          # no-op, no launch
+    assert f(h, None, 4, y, None, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert f(h, x, 4, None, None, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert f(h, x, 4, x, None, None) == pkg.LMOE_ERR_INVALID_ARG      # y == x
+    assert f(h, x, 4, x + 2 * D, None, None) == pkg.LMOE_ERR_INVALID_ARG  # overlap
+    assert f(h, x + 2, 4, y, None, None) == pkg.LMOE_ERR_INVALID_ARG  # misaligned
+    bad_taps = pkg.LmoeTaps(None, FAKE + 8, None, None, None)
+    assert f(h, x, 4, y, None, ctypes.byref(bad_taps)) == pkg.LMOE_ERR_INVALID_ARG
+    r = lib.lmoe_route
+    assert r(None, FAKE, 4, FAKE, FAKE, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert r(h, FAKE, 65, FAKE, FAKE, None) == pkg.LMOE_ERR_TOO_MANY_TOKENS
+    assert r(h, FAKE, 0, FAKE, FAKE, None) == pkg.LMOE_OK
+    assert r(h, None, 4, FAKE, FAKE, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert r(h, FAKE, 4, FAKE + 4, FAKE, None) == pkg.LMOE_ERR_INVALID_ARG
+    lib.lmoe_destroy(h)
+
+
+def test_status_strings_and_stages(lib):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert lib.lmoe_status_string(s)
+    assert lib.lmoe_status_string(99) == b"unknown status"
+    names = pkg.stage_names()
+    assert names[0] == "proj_in" and "expert_up" in names and len(names) == lib.lmoe_num_stages()
+    assert lib.lmoe_stage_name(-1) is None
+    assert lib.lmoe_profile_begin(None, 4) == pkg.LMOE_ERR_INVALID_ARG
+    ms = (ctypes.c_float * 8)()
+    n = ctypes.c_int32()
+    assert lib.lmoe_profile_end(None, ms, 8, ctypes.byref(n)) == pkg.LMOE_ERR_INVALID_ARG
+
+
+def test_product_path_does_not_reach_the_oracle():
+    for dirpath, _, files in os.walk(os.path.join(ROOT, "sparse_moe_layer_latentmoe_amd")):
+        for fn in files:
+            if fn.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, fn), encoding="utf-8").read()
+                assert "oracle" not in text.replace("no oracle", ""), fn

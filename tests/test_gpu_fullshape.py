@@ -1,0 +1,65 @@
+"""Parity at the full layer shape (hidden 8192, latent 2048, 512 experts,
+top-22, expert MLP 2048->5120->2048, shared 8192->10240->8192), in the launch
+configuration the benchmark times: every token is checked against properties
+that hold at any size, and a seeded sample of tokens is checked against the
+oracle token by token (the layer is token-wise, so a sampled row's oracle
+output needs only that row)."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import lmoe_inputs as li
+import sparse_moe_layer_latentmoe_amd as pkg
+from parity import assert_parity, check_properties, compare, run_gpu, weight_dict
+
+pytestmark = [pytest.mark.gpu, pytest.mark.fullshape]
+
+SAMPLE = 6
+
+
+@pytest.fixture(scope="module")
+def full():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    dev = torch.device("cuda:0")
+    wl = li.workload("decode")
+    w = li.make_weights(wl, dev)
+    print("[full-shape weights generated]", flush=True)
+    return dev, w
+
+
+def sample_rows(T, seed):
+    rng = np.random.default_rng(seed)
+    rows = {0, T - 1} | set(rng.choice(T, size=min(T, SAMPLE) - 2 if T > 2 else 0,
+                                       replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", ["decode", "mtp_verify", "prefill", "skewed"])
+def test_full_shape(full, name):
+    dev, w = full
+    wl = li.workload(name)
+    print(f"[full {name} T={wl.tokens}]", flush=True)
+    weights = dict(w)
+    if wl.bias_recipe == "zipf":
+        weights["router_bias"] = torch.from_numpy(
+            li.zipf_bias(wl.shape, wl.seed + 3, wl.zipf_s, wl.zipf_dead_frac)).to(dev)
+    inp = li.make_inputs(wl, dev, weights=weights)
+    layer = pkg.LatentMoE(wl.shape, weight_dict(inp), wl.tokens)
+    g = run_gpu(layer, inp.x)
+    check_properties(g, wl.shape, wl.tokens)
+    U = int((g.counts > 0).sum())
+    print(f"  unique experts {U}, empty {512 - U}, max load {g.counts.max()}", flush=True)
+    if name == "skewed":
+        assert 512 - U >= 51            # the dead experts never receive tokens
+        assert g.counts.max() >= wl.tokens * 0.9
+    rows = sample_rows(wl.tokens, 11)
+    rep = compare(g, li.bf16_bits(inp.x), li.HostWeights(inp), wl.shape, rows=rows)
+    print(f"  sampled rows {rows.tolist()}: {rep}", flush=True)
+    sys.stdout.flush()
+    assert_parity(rep)
+    del layer
+    torch.cuda.empty_cache()

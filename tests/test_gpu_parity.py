@@ -1,0 +1,222 @@
+"""GPU parity of the HIP LatentMoE layer against the CPU oracle, through the C
+ABI, at sizes the oracle finishes in seconds (several tiles and ragged
+tails), on both GEMM tilings, plus the edge cases of the method."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import lmoe_inputs as li
+import sparse_moe_layer_latentmoe_amd as pkg
+from parity import (MEDIUM, assert_parity, check_properties, compare, medium, oracle_config,
+                    run_gpu, weight_dict)
+from oracle import lmoe_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    return torch.device("cuda:0")
+
+
+def layer_for(wl, inp, path=pkg.PATH_AUTO, max_tokens=None):
+    return pkg.LatentMoE(wl.shape, weight_dict(inp), max_tokens or max(wl.tokens, 1), path)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.mark.parametrize("tokens", [64, 1, 17, 63])
+def test_tiny_matches_oracle(dev, tokens):
+    wl = li.workload("tiny", tokens=tokens)
+    say(f"[tiny T={tokens}]")
+    inp = li.make_inputs(wl, dev)
+    g = run_gpu(layer_for(wl, inp), inp.x)
+    check_properties(g, wl.shape, tokens)
+    rep = compare(g, li.bf16_bits(inp.x), li.HostWeights(inp, eager_experts=True), wl.shape)
+    say(rep)
+    assert_parity(rep)
+
+
+@pytest.mark.parametrize("path", [pkg.PATH_STREAM, pkg.PATH_TILED, pkg.PATH_AUTO])
+@pytest.mark.parametrize("tokens", [300, 129])
+def test_medium_both_tilings(dev, path, tokens):
+    wl = medium(tokens)
+    say(f"[medium T={tokens} path={path}]")
+    inp = li.make_inputs(wl, dev)
+    g = run_gpu(layer_for(wl, inp, path), inp.x)
+    check_properties(g, wl.shape, tokens)
+    rep = compare(g, li.bf16_bits(inp.x), li.HostWeights(inp, eager_experts=True), wl.shape)
+    say(rep)
+    assert_parity(rep)
+
+
+def test_paths_agree_on_routing(dev):
+    wl = medium(300)
+    inp = li.make_inputs(wl, dev)
+    a = run_gpu(layer_for(wl, inp, pkg.PATH_STREAM), inp.x)
+    b = run_gpu(layer_for(wl, inp, pkg.PATH_TILED), inp.x)
+    assert np.array_equal(a.idx, b.idx)
+    assert np.array_equal(a.z32, b.z32) or np.abs(a.z32 - b.z32).max() < 1e-4
+
+
+def test_zero_input(dev):
+    wl = li.workload("tiny")
+    inp = li.make_inputs(wl, dev)
+    inp.x.zero_()
+    g = run_gpu(layer_for(wl, inp), inp.x)
+    assert torch.count_nonzero(g.y) == 0
+    beta = inp.router_bias.cpu().numpy()
+    want = np.sort(np.argsort(-beta, kind="stable")[:wl.shape.num_experts_per_tok])
+    assert np.all(g.idx == want[None, :])
+
+
+def test_ties_go_to_lower_expert_index(dev):
+    wl = li.workload("tiny")
+    inp = li.make_inputs(wl, dev)
+    inp.x.zero_()                       # every score is sigmoid(0) = 0.5
+    bias = torch.zeros(wl.shape.n_routed_experts, dtype=torch.float32)
+    bias[[3, 7, 9, 12, 15]] = 0.25      # five equal winners for K = 4
+    inp.router_bias.copy_(bias.to(dev))
+    g = run_gpu(layer_for(wl, inp), inp.x)
+    assert np.all(g.idx == np.array([3, 7, 9, 12])[None, :])
+    assert np.all(g.w == np.float32(1.25))
+
+
+def test_one_expert_takes_every_token_and_empty_experts(dev):
+    wl = medium(300)
+    inp = li.make_inputs(wl, dev)
+    bias = inp.router_bias.clone()
+    bias[5] = 2.0                       # always selected
+    bias[10:20] = -2.0                  # never selected
+    inp.router_bias.copy_(bias)
+    for path in (pkg.PATH_STREAM, pkg.PATH_TILED):
+        g = run_gpu(layer_for(wl, inp, path), inp.x)
+        check_properties(g, wl.shape, 300)
+        assert g.counts[5] == 300 and np.all(g.counts[10:20] == 0)
+        rep = compare(g, li.bf16_bits(inp.x), li.HostWeights(inp, eager_experts=True), wl.shape)
+        say(path, rep)
+        assert_parity(rep)
+
+
+def test_single_expert_per_token_weight_is_rho(dev):
+    base = li.workload("tiny")
+    sh = li.LayerShape(256, 64, 16, 1, 128, 512, 5.0)
+    wl = li.Workload("tiny_k1", sh, 64)
+    inp = li.make_inputs(wl, dev)
+    g = run_gpu(layer_for(wl, inp), inp.x)
+    assert np.all(g.w == np.float32(5.0))
+    rep = compare(g, li.bf16_bits(inp.x), li.HostWeights(inp, eager_experts=True), sh)
+    assert_parity(rep)
+    del base
+
+
+def test_all_experts_per_token(dev):
+    sh = li.LayerShape(256, 64, 16, 16, 128, 512, 5.0)
+    wl = li.Workload("tiny_kE", sh, 40)
+    inp = li.make_inputs(wl, dev)
+    g = run_gpu(layer_for(wl, inp), inp.x)
+    assert np.all(g.idx == np.arange(16)[None, :])
+    rep = compare(g, li.bf16_bits(inp.x), li.HostWeights(inp, eager_experts=True), sh)
+    assert_parity(rep)
+
+
+def test_identical_experts_give_rho_times_one_expert(dev):
+    wl = medium(200)
+    inp = li.make_inputs(wl, dev)
+    inp.expert_up.copy_(inp.expert_up[7:8].expand_as(inp.expert_up))
+    inp.expert_down.copy_(inp.expert_down[7:8].expand_as(inp.expert_down))
+    for path in (pkg.PATH_STREAM, pkg.PATH_TILED):
+        g = run_gpu(layer_for(wl, inp, path), inp.x)
+        z = g.z32.astype(np.float64)
+        one = O.expert_mlp(z, O.bf16_bits_to_f64(li.bf16_bits(inp.expert_up[7])),
+                           O.bf16_bits_to_f64(li.bf16_bits(inp.expert_down[7])))
+        rel = np.abs(g.r - 5.0 * one).max() / np.abs(5.0 * one).max()
+        say(path, "identical experts rel", rel)
+        assert rel <= 2e-2
+
+
+def test_zero_expert_up_gives_shared_only(dev):
+    wl = medium(150)
+    inp = li.make_inputs(wl, dev)
+    inp.expert_up.zero_()
+    g = run_gpu(layer_for(wl, inp), inp.x)
+    assert np.count_nonzero(g.r) == 0
+    cfg = oracle_config(wl.shape)
+    hw = li.HostWeights(inp, eager_experts=True)
+    ref = O.shared_expert(O.bf16_bits_to_f64(li.bf16_bits(inp.x)),
+                          O.bf16_bits_to_f64(hw.shared_up), O.bf16_bits_to_f64(hw.shared_down))
+    y = g.y.float().cpu().numpy()
+    assert np.abs(y - ref).max() / np.abs(ref).max() <= 2e-2
+    del cfg
+
+
+def test_deterministic_and_token_order_equivariant(dev):
+    wl = medium(300)
+    inp = li.make_inputs(wl, dev)
+    for path in (pkg.PATH_STREAM, pkg.PATH_TILED):
+        layer = layer_for(wl, inp, path)
+        a = run_gpu(layer, inp.x)
+        b = run_gpu(layer, inp.x)
+        assert torch.equal(a.y, b.y) and np.array_equal(a.idx, b.idx)
+        perm = torch.randperm(300, generator=torch.Generator().manual_seed(4))
+        c = run_gpu(layer, inp.x[perm.to(dev)].contiguous())
+        assert torch.equal(c.y, a.y[perm.to(dev)])
+        assert np.array_equal(c.idx, a.idx[perm.numpy()])
+
+
+def test_smaller_batch_after_larger_on_one_handle(dev):
+    # the workspace keeps the larger batch's contents; the smaller batch
+    # (which may pick another tiling) must still match the oracle
+    wl = medium(300)
+    inp = li.make_inputs(wl, dev)
+    layer = layer_for(wl, inp, max_tokens=300)
+    run_gpu(layer, inp.x)
+    x = inp.x[:37].contiguous()
+    small = run_gpu(layer, x)
+    check_properties(small, wl.shape, 37)
+    rep = compare(small, li.bf16_bits(x), li.HostWeights(inp, eager_experts=True), wl.shape)
+    say(rep)
+    assert_parity(rep)
+
+
+def test_route_entry_point_on_oracle_latent(dev):
+    wl = medium(300)
+    inp = li.make_inputs(wl, dev)
+    cfg = oracle_config(wl.shape)
+    hw = li.HostWeights(inp, eager_experts=True)
+    ref = O.forward(li.bf16_bits(inp.x), hw, cfg)
+    layer = layer_for(wl, inp)
+    idx, w = layer.route(torch.from_numpy(ref["z32"]).to(dev))
+    idx = idx.cpu().numpy()
+    tie = ref["gap"] < 1e-6
+    assert np.array_equal(idx[~tie], ref["idx"][~tie])
+    assert np.abs(w.cpu().numpy()[~tie] - ref["w"][~tie]).max() <= 5e-5
+
+
+def test_zero_tokens_is_a_noop(dev):
+    wl = li.workload("tiny")
+    inp = li.make_inputs(wl, dev)
+    layer = layer_for(wl, inp)
+    y = torch.full((0, 256), 1.0, dtype=torch.bfloat16, device=dev)
+    layer.forward_into(inp.x[:0], y)
+    torch.cuda.synchronize()
+
+
+def test_profile_events_cover_every_stage(dev):
+    wl = li.workload("tiny")
+    inp = li.make_inputs(wl, dev)
+    layer = layer_for(wl, inp)
+    layer.profile_begin(3)
+    for _ in range(3):
+        layer.forward(inp.x)
+    stages, n = layer.profile_end()
+    assert n == 3 and set(stages) == set(pkg.stage_names())
+    assert all(v >= 0 for v in stages.values())
