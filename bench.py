@@ -38,7 +38,8 @@ def stage_work(sh, T, U):
     K, F, S = sh.num_experts_per_tok, sh.moe_intermediate_size, sh.moe_shared_expert_intermediate_size
     slots = T * K
     b = {
-        "proj_in": (R + S) * D * 2 + T * D * 2 + T * R * 6 + T * S * 2,
+        "proj_latent": R * D * 2 + T * D * 2 + T * R * 6,
+        "shared_up": S * D * 2 + T * D * 2 + T * S * 2,
         "router_logits": E * R * 4 + T * R * 4 + T * E * 4,
         "router_select": T * E * 4 + E * 4 + slots * 8,
         "dispatch": slots * 4 * 4 + E * 12,
@@ -48,7 +49,8 @@ def stage_work(sh, T, U):
         "proj_out": D * (R + S) * 2 + T * (R + S) * 2 + T * D * 2,
     }
     f = {
-        "proj_in": 2 * T * D * (R + S),
+        "proj_latent": 2 * T * D * R,
+        "shared_up": 2 * T * D * S,
         "router_logits": 2 * T * R * E,
         "router_select": 0, "dispatch": 0,
         "expert_up": 2 * slots * R * F,

@@ -31,6 +31,10 @@
  *    caller's next synchronisation.  Inputs must be finite.
  *  - one handle owns one workspace: do not use a handle on two streams at
  *    the same time.
+ *  - the first lmoe_forward on a handle creates one auxiliary HIP stream
+ *    (non-blocking, default priority) and two events, used to run the shared
+ *    expert's up projection concurrently with the router (forked from and
+ *    joined back into `stream`); lmoe_destroy releases them.
  */
 #ifndef LMOE_H
 #define LMOE_H
@@ -114,7 +118,8 @@ lmoe_status lmoe_forward(lmoe_handle *h, const uint16_t *x, int32_t T, uint16_t 
 lmoe_status lmoe_route(lmoe_handle *h, const float *z_f32, int32_t T, int32_t *topk_idx,
                        float *topk_w, void *stream);
 
-/* Free the handle (host memory only).  NULL is a no-op. */
+/* Free the handle and the auxiliary stream and events it created (no
+ * device memory is freed: the caller owns all of it).  NULL is a no-op. */
 void lmoe_destroy(lmoe_handle *h);
 
 /* Static text for a status code. */
@@ -122,7 +127,10 @@ const char *lmoe_status_string(lmoe_status s);
 
 /* ---- per-kernel timing (HIP events on the forward's stream) ------------ */
 
-/* Number of timed stages of lmoe_forward and the name of stage i. */
+/* Number of timed stages of lmoe_forward and the name of stage i.  Stages
+ * 0..7 run back to back on the forward's stream (the last one, proj_out,
+ * includes the wait for the auxiliary stream); stage 8 ("shared_up") is
+ * timed on the auxiliary stream and overlaps stages 0..6. */
 int32_t lmoe_num_stages(void);
 const char *lmoe_stage_name(int32_t i);
 

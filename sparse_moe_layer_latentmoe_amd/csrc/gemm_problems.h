@@ -12,9 +12,11 @@ namespace lmoe {
 
 // [z | Hs] = x [W1 ; Wsu]^T  (fc1_latent and the shared expert's up
 // projection share the input x; page "Nemotron 3 Ultra 架构深度拆解报告",
-// CH5 §5.6 Steps 5 and 7).  Columns n < R give the latent z, stored fp32
-// (router input) and bf16 (expert input); columns n >= R give the shared
-// expert's hidden relu(.)^2 in bf16.
+// CH5 §5.6 Steps 5 and 7).  Global column n < R gives the latent z, stored
+// fp32 (router input) and bf16 (expert input); n >= R gives the shared
+// expert's hidden relu(.)^2 in bf16.  One launch covers the columns
+// [noff, noff + ncount), so the latent and the shared part can run as two
+// launches on two streams (R is a multiple of every column block).
 struct ProjIn {
   const uint16_t* x;
   const uint16_t* w1;
@@ -23,21 +25,24 @@ struct ProjIn {
   uint16_t* z16;
   uint16_t* hs;
   int T, D, R, S;
-  __device__ int N() const { return R + S; }
-  __device__ int K() const { return D; }
-  __device__ int K0() const { return D; }
+  int noff, ncount;
+  __host__ __device__ int N() const { return ncount; }
+  __host__ __device__ int K() const { return D; }
+  __host__ __device__ int K0() const { return D; }
   __device__ const uint16_t* b_row0(int, int n) const {
-    return n < R ? w1 + (size_t)n * D : wsu + (size_t)(n - R) * D;
+    const int g = noff + n;
+    return g < R ? w1 + (size_t)g * D : wsu + (size_t)(g - R) * D;
   }
   __device__ const uint16_t* b_row1(int, int) const { return nullptr; }
   __device__ const uint16_t* a_row0(int m) const { return x + (size_t)m * D; }
   __device__ const uint16_t* a_row1(int) const { return nullptr; }
   __device__ void store(int, int m, int n, f32x4 v) const {
-    if (n < R) {
-      *reinterpret_cast<f32x4*>(z32 + (size_t)m * R + n) = v;
-      store4_bf16(z16 + (size_t)m * R + n, v);
+    const int g = noff + n;
+    if (g < R) {
+      *reinterpret_cast<f32x4*>(z32 + (size_t)m * R + g) = v;
+      store4_bf16(z16 + (size_t)m * R + g, v);
     } else {
-      store4_bf16_relu_sq(hs + (size_t)m * S + (n - R), v);
+      store4_bf16_relu_sq(hs + (size_t)m * S + (g - R), v);
     }
   }
 };
@@ -52,9 +57,9 @@ struct ProjOut {
   const uint16_t* wsd;
   uint16_t* y;
   int T, D, R, S;
-  __device__ int N() const { return D; }
-  __device__ int K() const { return R + S; }
-  __device__ int K0() const { return R; }
+  __host__ __device__ int N() const { return D; }
+  __host__ __device__ int K() const { return R + S; }
+  __host__ __device__ int K0() const { return R; }
   __device__ const uint16_t* b_row0(int, int n) const { return w2 + (size_t)n * R; }
   __device__ const uint16_t* b_row1(int, int n) const { return wsd + (size_t)n * S; }
   __device__ const uint16_t* a_row0(int m) const { return r16 + (size_t)m * R; }
@@ -72,9 +77,9 @@ struct ExpUp {
   const uint16_t* wup;  // [E, F, R]
   uint16_t* h;          // [slots, F]
   int R, F;
-  __device__ int N() const { return F; }
-  __device__ int K() const { return R; }
-  __device__ int K0() const { return R; }
+  __host__ __device__ int N() const { return F; }
+  __host__ __device__ int K() const { return R; }
+  __host__ __device__ int K0() const { return R; }
   __device__ const uint16_t* b_row0(int e, int n) const {
     return wup + ((size_t)e * F + n) * R;
   }
@@ -93,9 +98,9 @@ struct ExpDown {
   const uint16_t* wdn;  // [E, R, F]
   uint16_t* o;          // [slots, R]
   int R, F;
-  __device__ int N() const { return R; }
-  __device__ int K() const { return F; }
-  __device__ int K0() const { return F; }
+  __host__ __device__ int N() const { return R; }
+  __host__ __device__ int K() const { return F; }
+  __host__ __device__ int K0() const { return F; }
   __device__ const uint16_t* b_row0(int e, int n) const {
     return wdn + ((size_t)e * R + n) * F;
   }

@@ -7,12 +7,12 @@
 // exactly once, with many 16-byte loads in flight per wave, and turned into
 // MFMA operands straight from registers (no LDS staging of weights).
 //
-// Work-group = NW waves on one block of 64 weight rows (4 MFMA row groups of
-// 16) and MT*16 token rows.  The k range is split evenly over the NW waves
-// (so many waves stream disjoint parts of the same rows); each wave keeps a
-// double-buffered register pipeline of 2 x (4 weight + MT activation)
-// fragments per 32-wide k step, then the waves' partial sums are added in
-// LDS in a fixed order (deterministic) and the problem's epilogue stores.
+// Work-group = NW waves on one block of RG*16 weight rows (RG MFMA row
+// groups of 16) and MT*16 token rows.  The k range is split evenly over the
+// NW waves (so many waves stream disjoint parts of the same rows); each wave
+// keeps a double-buffered register pipeline of U k steps of (RG weight + MT
+// activation) fragments, then the waves' partial sums are added in LDS in a
+// fixed order (deterministic) and the problem's epilogue stores.
 //
 // Weights are the MFMA A operand (rows = output columns n), activations the
 // B operand (columns = tokens), so each lane ends with four consecutive
@@ -22,10 +22,9 @@
 
 namespace lmoe {
 
-constexpr int kRG = 4;   // 16-row groups of weights per work-group (64 rows)
-constexpr int kU = 2;    // k steps of 32 per pipeline stage
-
-template <class P, bool GROUPED, int NW, int MT>
+// NT: load weights with the non-temporal hint (kept for measurement; the
+// launch shapes below use plain loads).
+template <class P, bool GROUPED, int NW, int MT, int kRG, int kU, bool NT>
 __global__ __launch_bounds__(NW * 64) void stream_gemm_kernel(P p, int mrows, const Tile* tiles,
                                                               const int* ntiles) {
   constexpr int J = kRG * MT;
@@ -91,7 +90,10 @@ __global__ __launch_bounds__(NW * 64) void stream_gemm_kernel(P p, int mrows, co
 #pragma unroll
     for (int u = 0; u < kU; ++u)
 #pragma unroll
-      for (int g = 0; g < kRG; ++g) wf[u][g] = load8_stream((s0 ? b0[g] : b1[g]) + kk + u * 32);
+      for (int g = 0; g < kRG; ++g) {
+        const uint16_t* q = (s0 ? b0[g] : b1[g]) + kk + u * 32;
+        wf[u][g] = NT ? load8_stream(q) : load8(q);
+      }
 #pragma unroll
     for (int u = 0; u < kU; ++u)
 #pragma unroll
@@ -143,71 +145,82 @@ __global__ __launch_bounds__(NW * 64) void stream_gemm_kernel(P p, int mrows, co
   }
 }
 
-// Waves per work-group: the fewest that still give about two waves per
-// SIMD over the whole launch, subject to the k range splitting evenly into
-// 64-wide pipeline stages (and the segment boundary falling on one).
-static int pick_nw(int K, int K0, long blocks) {
-  const int opts[4] = {1, 2, 4, 8};
-  int best = 1;
-  for (int i = 0; i < 4; ++i) {
-    const int nw = opts[i];
-    if (K % (nw * 32 * kU) != 0) continue;
-    best = nw;
-    if (blocks * nw >= 2048) break;
-  }
-  (void)K0;
-  return best;
+// Launch shapes.  Measured on MI355X with the full-shape decode problems
+// (T = 32, ~400 touched experts): plain loads beat the non-temporal hint for
+// this access pattern (each wave instruction touches half of 16 cache lines,
+// and the other half is wanted by the next instruction), and the shapes
+// below were the fastest of a sweep over waves/work-group, row groups and
+// pipeline depth.  A shape is used only if it divides the problem; the
+// chain ends in one that always does (dimensions are multiples of 64).
+struct Shape {
+  int nw, rg, u;
+};
+
+static bool fits(const Shape& c, int N, int K, int K0) {
+  return K % (c.nw * 32 * c.u) == 0 && K0 % (32 * c.u) == 0 && N % (16 * c.rg) == 0;
+}
+
+static Shape pick(const Shape& pref, int N, int K, int K0) {
+  const Shape chain[] = {pref, {4, 2, 2}, {2, 2, 2}, {1, 2, 2}, {1, 1, 2}};
+  for (const Shape& c : chain)
+    if (fits(c, N, K, K0)) return c;
+  return {1, 1, 2};
 }
 
 template <class P, bool GROUPED, int MT>
-static hipError_t launch_mt(const P& p, int nw, long grid, int mrows, const Tile* tiles,
-                            const int* ntiles, hipStream_t s) {
+static hipError_t launch_shape(const P& p, const Shape& c, long mtiles, int mrows, const Tile* tiles,
+                               const int* ntiles, hipStream_t s) {
+  const long grid = mtiles * (p.N() / (16 * c.rg));
   if (grid <= 0) return hipSuccess;
-  switch (nw) {
-    case 1: stream_gemm_kernel<P, GROUPED, 1, MT><<<grid, 64, 0, s>>>(p, mrows, tiles, ntiles); break;
-    case 2: stream_gemm_kernel<P, GROUPED, 2, MT><<<grid, 128, 0, s>>>(p, mrows, tiles, ntiles); break;
-    case 4: stream_gemm_kernel<P, GROUPED, 4, MT><<<grid, 256, 0, s>>>(p, mrows, tiles, ntiles); break;
-    default: stream_gemm_kernel<P, GROUPED, 8, MT><<<grid, 512, 0, s>>>(p, mrows, tiles, ntiles); break;
+#define LMOE_SG(NW_, RG_, U_)                                                              \
+  if (c.nw == NW_ && c.rg == RG_ && c.u == U_) {                                           \
+    stream_gemm_kernel<P, GROUPED, NW_, MT, RG_, U_, false>                                \
+        <<<grid, NW_ * 64, 0, s>>>(p, mrows, tiles, ntiles);                               \
+    return hipGetLastError();                                                              \
   }
-  return hipGetLastError();
+  LMOE_SG(4, 4, 2)
+  LMOE_SG(4, 4, 4)
+  LMOE_SG(8, 2, 4)
+  LMOE_SG(4, 2, 2)
+  LMOE_SG(2, 2, 2)
+  LMOE_SG(1, 2, 2)
+  LMOE_SG(1, 1, 2)
+#undef LMOE_SG
+  return hipErrorInvalidConfiguration;
 }
 
 template <class P>
-static hipError_t launch_dense(const P& p, int N, int K, int K0, int T, hipStream_t s) {
+static hipError_t launch_dense(const P& p, const Shape& pref, int T, hipStream_t s) {
   const int mt = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
   const long mtiles = (T + 16 * mt - 1) / (16 * mt);
-  const long nblocks = N / (16 * kRG);
-  const long grid = mtiles * nblocks;
-  const int nw = pick_nw(K, K0, grid);
+  const Shape c = pick(pref, p.N(), p.K(), p.K0());
   switch (mt) {
-    case 1: return launch_mt<P, false, 1>(p, nw, grid, T, nullptr, nullptr, s);
-    case 2: return launch_mt<P, false, 2>(p, nw, grid, T, nullptr, nullptr, s);
-    default: return launch_mt<P, false, 4>(p, nw, grid, T, nullptr, nullptr, s);
+    case 1: return launch_shape<P, false, 1>(p, c, mtiles, T, nullptr, nullptr, s);
+    case 2: return launch_shape<P, false, 2>(p, c, mtiles, T, nullptr, nullptr, s);
+    default: return launch_shape<P, false, 4>(p, c, mtiles, T, nullptr, nullptr, s);
   }
 }
 
 template <class P>
-static hipError_t launch_grouped(const P& p, int N, int K, const Tile* tiles, const int* ntiles,
-                                 int max_tiles, hipStream_t s) {
-  const long nblocks = N / (16 * kRG);
-  const long grid = (long)max_tiles * nblocks;
-  const int nw = pick_nw(K, K, grid);
-  return launch_mt<P, true, 1>(p, nw, grid, 0, tiles, ntiles, s);
+static hipError_t launch_grouped(const P& p, const Shape& pref, const Tile* tiles,
+                                 const int* ntiles, int max_tiles, hipStream_t s) {
+  const Shape c = pick(pref, p.N(), p.K(), p.K0());
+  return launch_shape<P, true, 1>(p, c, max_tiles, 0, tiles, ntiles, s);
 }
 
 hipError_t stream_proj_in(const ProjIn& p, hipStream_t s) {
-  return launch_dense(p, p.R + p.S, p.D, p.D, p.T, s);
+  return launch_dense(p, Shape{4, 4, 2}, p.T, s);
 }
 hipError_t stream_proj_out(const ProjOut& p, hipStream_t s) {
-  return launch_dense(p, p.D, p.R + p.S, p.R, p.T, s);
+  return launch_dense(p, Shape{4, 2, 2}, p.T, s);
 }
 hipError_t stream_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, int max_tiles,
                          hipStream_t s) {
-  return launch_grouped(p, p.F, p.R, tiles, ntiles, max_tiles, s);
+  return launch_grouped(p, Shape{4, 4, 4}, tiles, ntiles, max_tiles, s);
 }
 hipError_t stream_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles, int max_tiles,
                            hipStream_t s) {
-  return launch_grouped(p, p.R, p.F, tiles, ntiles, max_tiles, s);
+  return launch_grouped(p, Shape{8, 2, 4}, tiles, ntiles, max_tiles, s);
 }
 
 }  // namespace lmoe

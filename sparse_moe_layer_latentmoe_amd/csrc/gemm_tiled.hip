@@ -148,7 +148,7 @@ static hipError_t launch_grouped(const P& p, int N, const Tile* tiles, const int
 int tiled_block_m() { return kBM; }
 int tiled_block_n() { return kBN; }
 
-hipError_t tiled_proj_in(const ProjIn& p, hipStream_t s) { return launch_dense(p, p.R + p.S, p.T, s); }
+hipError_t tiled_proj_in(const ProjIn& p, hipStream_t s) { return launch_dense(p, p.ncount, p.T, s); }
 hipError_t tiled_proj_out(const ProjOut& p, hipStream_t s) { return launch_dense(p, p.D, p.T, s); }
 hipError_t tiled_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, int max_tiles,
                         hipStream_t s) {

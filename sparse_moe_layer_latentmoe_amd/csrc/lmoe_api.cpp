@@ -1,9 +1,9 @@
 // C ABI of the LatentMoE layer: argument checks, workspace carving and the
 // launch sequence of one forward pass.  See include/lmoe.h for the contract.
 //
-// Launch sequence (one stream, no host synchronisation; page "Nemotron 3
-// Ultra 架构深度拆解报告", CH5 §5.6 Steps 1-7):
-//   proj_in        x -> z (fp32 + bf16) and the shared expert's relu^2 hidden
+// Launch sequence (no host synchronisation; page "Nemotron 3 Ultra 架构深度
+// 拆解报告", CH5 §5.6 Steps 1-7).  On the caller's stream:
+//   proj_latent    x -> z (fp32 + bf16)                        (Step 5)
 //   router_logits  z (fp32) -> logits                          (Step 1)
 //   router_select  logits -> top-K experts and weights         (Steps 2-4)
 //   dispatch       experts -> expert-sorted rows + tile list   (Step 6 grouping)
@@ -11,6 +11,11 @@
 //   expert_down    H Wdn[e]^T                                  (Step 6)
 //   combine        r = sum_k w O                               (Step 6 index_add_)
 //   proj_out       y = r W2^T + Hs Wsd^T                       (Step 7)
+// and, forked onto the handle's auxiliary stream right after the caller's
+// prior work and joined before proj_out (the shared expert only needs x):
+//   shared_up      x -> relu(x Wsu^T)^2                        (Step 7)
+// The router/dispatch chain is latency-bound and leaves HBM idle; the
+// shared expert's weight stream fills that time.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -28,10 +33,16 @@ using namespace lmoe;
 
 namespace {
 
-constexpr int kNumStages = 8;
-const char* const kStageNames[kNumStages] = {"proj_in",     "router_logits", "router_select",
-                                             "dispatch",    "expert_up",     "expert_down",
-                                             "combine",     "proj_out"};
+// Stages 0..7 run back to back on the caller's stream (stage i is timed
+// between events i and i + 1; proj_out's interval includes the wait for the
+// auxiliary stream); stage 8 runs on the auxiliary stream between its own
+// pair of events.
+constexpr int kNumStages = 9;
+constexpr int kMainStages = 8;
+constexpr int kEventsPerForward = kMainStages + 1 + 2;
+const char* const kStageNames[kNumStages] = {
+    "proj_latent", "router_logits", "router_select", "dispatch", "expert_up",
+    "expert_down", "combine",       "proj_out",      "shared_up"};
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -39,9 +50,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool tiled_dims_ok(const lmoe_config& c) {
   const int bn = tiled_block_n();
-  return (c.moe_latent_size + c.moe_shared_expert_intermediate_size) % bn == 0 &&
-         c.hidden_size % bn == 0 && c.moe_intermediate_size % bn == 0 &&
-         c.moe_latent_size % bn == 0;
+  return c.moe_shared_expert_intermediate_size % bn == 0 && c.hidden_size % bn == 0 &&
+         c.moe_intermediate_size % bn == 0 && c.moe_latent_size % bn == 0;
 }
 
 lmoe_status check_config(const lmoe_config* c) {
@@ -114,6 +124,9 @@ struct lmoe_handle {
   lmoe_weights w;
   char* ws;
   Layout L;
+  // auxiliary stream and its fork/join events, created by the first forward
+  hipStream_t aux = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
   // profiling
   int prof_max = 0, prof_n = 0;
   std::vector<hipEvent_t> events;
@@ -158,6 +171,9 @@ lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, void* wor
 void lmoe_destroy(lmoe_handle* h) {
   if (!h) return;
   for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
+  if (h->fork) (void)hipEventDestroy(h->fork);
+  if (h->join) (void)hipEventDestroy(h->join);
+  if (h->aux) (void)hipStreamDestroy(h->aux);
   delete h;
 }
 
@@ -182,7 +198,7 @@ const char* lmoe_stage_name(int32_t i) {
 lmoe_status lmoe_profile_begin(lmoe_handle* h, int32_t max_forwards) {
   if (!h || max_forwards <= 0 || max_forwards > 4096) return LMOE_ERR_INVALID_ARG;
   for (hipEvent_t e : h->events) (void)hipEventDestroy(e);
-  h->events.assign(static_cast<size_t>(max_forwards) * (kNumStages + 1), nullptr);
+  h->events.assign(static_cast<size_t>(max_forwards) * kEventsPerForward, nullptr);
   for (auto& e : h->events)
     if (hipEventCreate(&e) != hipSuccess) {
       e = nullptr;
@@ -198,14 +214,17 @@ lmoe_status lmoe_profile_end(lmoe_handle* h, float* ms, int32_t n_stages, int32_
   for (int i = 0; i < kNumStages; ++i) ms[i] = 0.f;
   lmoe_status st = LMOE_OK;
   for (int f = 0; f < h->prof_n && st == LMOE_OK; ++f) {
-    hipEvent_t* ev = &h->events[static_cast<size_t>(f) * (kNumStages + 1)];
-    if (hipEventSynchronize(ev[kNumStages]) != hipSuccess) {
+    hipEvent_t* ev = &h->events[static_cast<size_t>(f) * kEventsPerForward];
+    if (hipEventSynchronize(ev[kMainStages]) != hipSuccess ||
+        hipEventSynchronize(ev[kEventsPerForward - 1]) != hipSuccess) {
       st = LMOE_ERR_HIP;
       break;
     }
     for (int i = 0; i < kNumStages; ++i) {
       float t = 0.f;
-      if (hipEventElapsedTime(&t, ev[i], ev[i + 1]) != hipSuccess) {
+      hipEvent_t a = i < kMainStages ? ev[i] : ev[kMainStages + 1];
+      hipEvent_t b = i < kMainStages ? ev[i + 1] : ev[kMainStages + 2];
+      if (hipEventElapsedTime(&t, a, b) != hipSuccess) {
         st = LMOE_ERR_HIP;
         break;
       }
@@ -289,9 +308,15 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   uint16_t* O = h->at<uint16_t>(h->L.o);
   uint16_t* r16 = h->at<uint16_t>(h->L.r16);
 
+  if (!h->aux) {
+    if (hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&h->join, hipEventDisableTiming) != hipSuccess)
+      return LMOE_ERR_HIP;
+  }
   hipEvent_t* ev = nullptr;
   if (h->prof_n < h->prof_max)
-    ev = &h->events[static_cast<size_t>(h->prof_n++) * (kNumStages + 1)];
+    ev = &h->events[static_cast<size_t>(h->prof_n++) * kEventsPerForward];
   int stage = 0;
   auto mark = [&]() -> bool {
     if (!ev) return true;
@@ -299,9 +324,20 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   };
   auto ok = [](hipError_t e) { return e == hipSuccess; };
 
+  // fork: the shared expert's up projection on the auxiliary stream
+  if (!ok(hipEventRecord(h->fork, s)) || !ok(hipStreamWaitEvent(h->aux, h->fork, 0)))
+    return LMOE_ERR_HIP;
+  if (ev && !ok(hipEventRecord(ev[kMainStages + 1], h->aux))) return LMOE_ERR_HIP;
+  ProjIn pshared{x, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, R, S};
+  if (!ok(dense_tiled ? tiled_proj_in(pshared, h->aux) : stream_proj_in(pshared, h->aux)))
+    return LMOE_ERR_HIP;
+  if (ev && !ok(hipEventRecord(ev[kMainStages + 2], h->aux))) return LMOE_ERR_HIP;
+  if (!ok(hipEventRecord(h->join, h->aux))) return LMOE_ERR_HIP;
+
   if (!mark()) return LMOE_ERR_HIP;
-  ProjIn pin{x, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S};
-  if (!ok(dense_tiled ? tiled_proj_in(pin, s) : stream_proj_in(pin, s))) return LMOE_ERR_HIP;
+  ProjIn platent{x, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, 0, R};
+  if (!ok(dense_tiled ? tiled_proj_in(platent, s) : stream_proj_in(platent, s)))
+    return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
   if (!ok(router_logits(z32, h->w.router, logits, T, E, R, s))) return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
@@ -325,6 +361,8 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   if (!ok(combine(O, inv, tw, T, K, R, r16, taps ? taps->r_latent : nullptr, s)))
     return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
+  // join, then y = r W2^T + Hs Wsd^T
+  if (!ok(hipStreamWaitEvent(s, h->join, 0))) return LMOE_ERR_HIP;
   ProjOut pout{r16, hs, h->w.fc2_latent, h->w.shared_down, y, T, D, R, S};
   if (!ok(dense_tiled ? tiled_proj_out(pout, s) : stream_proj_out(pout, s))) return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;

@@ -147,12 +147,12 @@ def test_status_strings_and_stages(lib):
         assert lib.lmoe_status_string(s)
     assert lib.lmoe_status_string(99) == b"unknown status"
     names = pkg.stage_names()
-    assert names[0] == "proj_in" and "expert_up" in names and len(names) == lib.lmoe_num_stages()
+    assert names[0] == "proj_latent" and "expert_up" in names and "shared_up" in names and len(names) == lib.lmoe_num_stages()
     assert lib.lmoe_stage_name(-1) is None
     assert lib.lmoe_profile_begin(None, 4) == pkg.LMOE_ERR_INVALID_ARG
-    ms = (ctypes.c_float * 8)()
+    ms = (ctypes.c_float * 16)()
     n = ctypes.c_int32()
-    assert lib.lmoe_profile_end(None, ms, 8, ctypes.byref(n)) == pkg.LMOE_ERR_INVALID_ARG
+    assert lib.lmoe_profile_end(None, ms, 16, ctypes.byref(n)) == pkg.LMOE_ERR_INVALID_ARG
 
 
 def test_product_path_does_not_reach_the_oracle():
