@@ -97,7 +97,9 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
       t.expert = e;
       t.row0 = off + i * tile_m;
       t.nrows = min(tile_m, n - i * tile_m);
-      t.pad = 0;
+      t.first = toff;
+      t.count = nt;
+      t.pad0 = t.pad1 = t.pad2 = 0;
       tiles[toff + i] = t;
     }
   }

@@ -4,7 +4,10 @@
 // with A the activations (row m) and B a weight stored out x in (row n), both
 // contiguous along k, and fp32 accumulation.  A problem says where row m of A
 // and row n of B start, for up to two consecutive k segments (k < K0 and
-// k >= K0), and what the epilogue stores for four consecutive columns.
+// k >= K0), the segment bases and row strides of A when its rows are strided
+// (a_base*/lda*; a_row*(m) == a_base*() + m * lda*()), and otherwise gathered
+// (kGatherA), the row strides of B (ldb*), and what the epilogue stores for
+// four consecutive columns.
 #pragma once
 #include "lmoe_device.h"
 
@@ -26,6 +29,13 @@ struct ProjIn {
   uint16_t* hs;
   int T, D, R, S;
   int noff, ncount;
+  static constexpr bool kGatherA = false;
+  __device__ const uint16_t* a_base0() const { return x; }
+  __device__ const uint16_t* a_base1() const { return x; }
+  __device__ long lda0() const { return D; }
+  __device__ long lda1() const { return D; }
+  __device__ long ldb0() const { return D; }
+  __device__ long ldb1() const { return D; }
   __host__ __device__ int N() const { return ncount; }
   __host__ __device__ int K() const { return D; }
   __host__ __device__ int K0() const { return D; }
@@ -57,6 +67,13 @@ struct ProjOut {
   const uint16_t* wsd;
   uint16_t* y;
   int T, D, R, S;
+  static constexpr bool kGatherA = false;
+  __device__ const uint16_t* a_base0() const { return r16; }
+  __device__ const uint16_t* a_base1() const { return hs; }
+  __device__ long lda0() const { return R; }
+  __device__ long lda1() const { return S; }
+  __device__ long ldb0() const { return R; }
+  __device__ long ldb1() const { return S; }
   __host__ __device__ int N() const { return D; }
   __host__ __device__ int K() const { return R + S; }
   __host__ __device__ int K0() const { return R; }
@@ -77,6 +94,13 @@ struct ExpUp {
   const uint16_t* wup;  // [E, F, R]
   uint16_t* h;          // [slots, F]
   int R, F;
+  static constexpr bool kGatherA = true;
+  __device__ const uint16_t* a_base0() const { return z16; }
+  __device__ const uint16_t* a_base1() const { return z16; }
+  __device__ long lda0() const { return R; }
+  __device__ long lda1() const { return R; }
+  __device__ long ldb0() const { return R; }
+  __device__ long ldb1() const { return R; }
   __host__ __device__ int N() const { return F; }
   __host__ __device__ int K() const { return R; }
   __host__ __device__ int K0() const { return R; }
@@ -98,6 +122,13 @@ struct ExpDown {
   const uint16_t* wdn;  // [E, R, F]
   uint16_t* o;          // [slots, R]
   int R, F;
+  static constexpr bool kGatherA = false;
+  __device__ const uint16_t* a_base0() const { return h; }
+  __device__ const uint16_t* a_base1() const { return h; }
+  __device__ long lda0() const { return F; }
+  __device__ long lda1() const { return F; }
+  __device__ long ldb0() const { return F; }
+  __device__ long ldb1() const { return F; }
   __host__ __device__ int N() const { return R; }
   __host__ __device__ int K() const { return F; }
   __host__ __device__ int K0() const { return F; }

@@ -31,8 +31,20 @@ __global__ __launch_bounds__(NW * 64) void stream_gemm_kernel(P p, int mrows, co
   __shared__ f32x4 red[NW > 1 ? NW : 1][J][64];
 
   const int nblocks = p.N() / (16 * kRG);
-  const int nb = blockIdx.x % nblocks;
-  const int tm = blockIdx.x / nblocks;
+  int nb, tm;
+  if (GROUPED) {
+    nb = blockIdx.x % nblocks;
+    tm = blockIdx.x / nblocks;
+  } else {
+    // Dense: the m tiles that share a weight block run back to back on one
+    // XCD (work-groups are dealt to the 8 XCDs round-robin by id), so the
+    // block is fetched from HBM once and re-read from that XCD's L2.
+    const int mtiles = (mrows + 16 * MT - 1) / (16 * MT);
+    const int local = blockIdx.x / 8;
+    tm = local % mtiles;
+    nb = (local / mtiles) * 8 + blockIdx.x % 8;
+    if (nb >= nblocks) return;
+  }
   int e = 0, m0, mcount;
   if (GROUPED) {
     if (tm >= *ntiles) return;
@@ -170,7 +182,8 @@ static Shape pick(const Shape& pref, int N, int K, int K0) {
 template <class P, bool GROUPED, int MT>
 static hipError_t launch_shape(const P& p, const Shape& c, long mtiles, int mrows, const Tile* tiles,
                                const int* ntiles, hipStream_t s) {
-  const long grid = mtiles * (p.N() / (16 * c.rg));
+  const long nblocks = p.N() / (16 * c.rg);
+  const long grid = GROUPED ? mtiles * nblocks : 8 * mtiles * ((nblocks + 7) / 8);
   if (grid <= 0) return hipSuccess;
 #define LMOE_SG(NW_, RG_, U_)                                                              \
   if (c.nw == NW_ && c.rg == RG_ && c.u == U_) {                                           \

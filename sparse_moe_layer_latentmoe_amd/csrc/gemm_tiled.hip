@@ -1,162 +1,287 @@
 // LDS-tiled bf16 MFMA GEMM for large token counts (prefill-sized batches),
 // where the layer is bound by matrix-core throughput.
 //
-// Work-group tile: 128 token rows x 128 weight rows, k in steps of 64.  Four
-// waves in a 2 x 2 arrangement each own a 64 x 64 sub-tile (4 x 4 MFMA
-// 16x16x32 tiles, 64 fp32 accumulators per lane).  Global -> register
-// prefetch of the next k tile overlaps the MFMAs of the current one; tiles
-// are double-buffered in LDS, one barrier per k tile.  LDS rows are padded
-// by 16 bytes so the 16 rows read by one MFMA fragment land in distinct banks.
+// Work-group tile: BM token rows x BN weight rows, k in steps of BK.  Eight
+// waves (2 along tokens x 4 along weights) each own a (BM/2) x (BN/4)
+// sub-tile of MFMA 16x16x32 tiles.  Two waves per SIMD are needed: measured
+// on MI355X, one wave per SIMD issuing independent 16x16x32 bf16 MFMAs back
+// to back reaches about half of the matrix-core peak, two reach ~90%.
 //
-// Grouped mode (experts): the m tiles come from the expert tile list built by
-// the dispatch kernel; a tile never spans two experts, rows past the tile's
-// count are zero-filled on load and masked on store.
+// Operands move global -> LDS with gfx950's direct 16-byte loads
+// (global_load_lds_dwordx4), NS stages in flight and no staging registers;
+// the LDS rows are XOR-swizzled so the 16 rows of an MFMA fragment read
+// fall in distinct banks (measured: zero bank conflicts).  Each k tile: wait
+// for this tile's loads, one barrier, all fragment reads, the next stage's
+// loads, then the MFMAs.
+//
+// Work order is XCD-aware (see work_item).  Grouped mode (experts) takes the
+// m tiles from the expert tile list built by the dispatch kernel; a tile
+// never spans two experts.
 #include "gemm_problems.h"
 #include "kernels.h"
 
 namespace lmoe {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64, kLDK = kBK + 8;
+// s_waitcnt with only the vector-memory counter set to N (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt and lgkmcnt left at their maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
-template <class P, bool GROUPED>
-__global__ __launch_bounds__(256) void tiled_gemm_kernel(P p, int mrows, const Tile* tiles,
-                                                         const int* ntiles) {
-  __shared__ uint16_t sA[2][kBM * kLDK];
-  __shared__ uint16_t sB[2][kBN * kLDK];
+// Workgroup barrier without a memory fence: the direct-to-LDS loads are
+// waited for explicitly (wait_vmcnt) so that later stages stay in flight.
+// The signal fences keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
-  const int nblocks = p.N() / kBN;
-  const int nb = blockIdx.x % nblocks;
-  const int tm = blockIdx.x / nblocks;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Work-item order.  Work-groups are dealt to the 8 XCDs round-robin by id,
+// and each XCD has its own L2, so XCD x is given the contiguous chunk x of
+// the work list: the work-groups resident on one XCD at a time are then
+// neighbours in the list and share operand panels in that XCD's L2 while
+// they walk k in step.  List order: for the grouped expert GEMMs, expert by
+// expert, n block by n block, the expert's m tiles fastest (they share the
+// weight panel); for dense GEMMs, groups of kDenseGroupM m tiles, m fastest.
+constexpr int kXcds = 8;
+constexpr int kDenseGroupM = 4;
+
+template <bool GROUPED>
+__device__ __forceinline__ bool work_item(int nblocks, int mrows, int bm, const Tile* tiles,
+                                          const int* ntiles, int& tm, int& nb) {
+  const int mtiles = GROUPED ? *ntiles : (mrows + bm - 1) / bm;
+  const int total = mtiles * nblocks;
+  const int chunk = (total + kXcds - 1) / kXcds;
+  const int local = blockIdx.x / kXcds;
+  const int item = (blockIdx.x % kXcds) * chunk + local;
+  if (local >= chunk || item >= total) return false;
+  if (GROUPED) {
+    const Tile t = tiles[item / nblocks];
+    const int i = item - t.first * nblocks;
+    nb = i / t.count;
+    tm = t.first + i % t.count;
+  } else {
+    const int gsz = kDenseGroupM * nblocks;
+    const int g = item / gsz;
+    const int gm = min(kDenseGroupM, mtiles - g * kDenseGroupM);
+    const int r = item - g * gsz;
+    tm = g * kDenseGroupM + r % gm;
+    nb = r / gm;
+  }
+  return true;
+}
+
+// Multi-stage variant: global -> LDS with gfx950's 16-byte direct loads
+// (global_load_lds_dwordx4), NS stages in flight, no staging registers.
+// A stage holds BM token rows then BN weight rows of BK bf16 each.  One wave
+// instruction moves 1 KB = 1024 / (2 BK) rows; lane l fills slot l % CPR of
+// row l / CPR and fetches the global chunk (slot ^ swz(row)) so the stage is
+// already swizzled.  Token rows past the tile's count are loaded from the
+// tile's first row instead (their outputs are never stored, and each output
+// row depends only on its own token row).
+template <class P, bool GROUPED, int BM, int BN, int BK, int NS, int WGN>
+__global__ __launch_bounds__(128 * WGN) void tiled_gemm_kernel(P p, int mrows, const Tile* tiles,
+                                                               const int* ntiles) {
+  constexpr int NW = 2 * WGN;            // waves: 2 along tokens x WGN along weights
+  constexpr int TM = BM / 32;            // 16-row token groups per wave
+  constexpr int TN = BN / (16 * WGN);    // 16-row weight groups per wave
+  constexpr int CPR = BK / 8;            // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;          // rows per wave instruction
+  constexpr int RPB = 256 / (BK * 2);    // rows per 256-byte bank window
+  constexpr int NIA = BM / RPI / NW;     // A instructions per wave per stage
+  constexpr int NIB = BN / RPI / NW;
+  constexpr int NI = NIA + NIB;
+  constexpr int SROWS = BM + BN;
+  static_assert((BM / RPI) % NW == 0 && (BN / RPI) % NW == 0, "rows per stage");
+  static_assert((NS - 2) * NI < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS][SROWS * BK];
+
+  int tm, nb;
+  if (!work_item<GROUPED>(p.N() / BN, mrows, BM, tiles, ntiles, tm, nb)) return;
   int e = 0, m0, mcount;
   if (GROUPED) {
-    if (tm >= *ntiles) return;
     const Tile t = tiles[tm];
     e = t.expert;
     m0 = t.row0;
     mcount = t.nrows;
   } else {
-    m0 = tm * kBM;
-    mcount = min(kBM, mrows - m0);
+    m0 = tm * BM;
+    mcount = min(BM, mrows - m0);
   }
-  const int n0 = nb * kBN;
+  const int n0 = nb * BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int K = p.K(), K0 = p.K0();
-  const int nk = K / kBK;
+  const int nk = K / BK;
 
-  // Global load assignment: 16-byte chunk c = tid + 256 j, row c / 8,
-  // k offset (c % 8) * 8; eight lanes cover one 128-byte row segment.
-  const int lrow = tid >> 3;
-  const int lk = (tid & 7) * 8;
-  const uint16_t* ga0[4];
-  const uint16_t* ga1[4];
-  const uint16_t* gb0[4];
-  const uint16_t* gb1[4];
+  auto swz = [](int row) { return (row / RPB) & (CPR - 1); };
+
+  // Per-lane source rows: instruction j of wave w covers stage rows
+  // RPI * (w + NW j) .. + RPI - 1; this lane takes row RPI * (w + NW j) + l / CPR.
+  // The swizzled chunk depends only on w and the lane (NW j RPI rows is a
+  // multiple of the swizzle period), so one chunk offset serves every j.
+  // Gathered token rows keep one pointer per instruction; strided rows are
+  // recomputed in issue() (no extra registers, no extra memory reads).
+  const int lr = lane / CPR;
+  const int chunk8 = ((lane % CPR) ^ swz(RPI * w + lr)) * 8;
+  constexpr bool GA = P::kGatherA;
+  const uint16_t* pa[GA ? NIA : 1];
+  if constexpr (GA) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = lrow + 32 * j;
-    const bool ok = row < mcount;
-    ga0[j] = ok ? p.a_row0(m0 + row) + lk : nullptr;
-    const uint16_t* q = ok ? p.a_row1(m0 + row) : nullptr;
-    ga1[j] = q ? q + lk : nullptr;
-    gb0[j] = p.b_row0(e, n0 + row) + lk;
-    q = p.b_row1(e, n0 + row);
-    gb1[j] = q ? q + lk : nullptr;
+    for (int j = 0; j < NIA; ++j) {
+      const int row = RPI * (w + NW * j) + lr;
+      pa[j] = p.a_row0(m0 + (row < mcount ? row : 0)) + chunk8;
+    }
   }
+  const uint16_t* pb0 = p.b_row0(e, n0 + RPI * w + lr) + chunk8;
+  const uint16_t* qb = p.b_row1(e, n0 + RPI * w + lr);
+  const uint16_t* pb1 = qb ? qb + chunk8 : nullptr;
+  const long sb0 = (long)RPI * NW * p.ldb0(), sb1 = (long)RPI * NW * p.ldb1();
 
-  bf16x8 ra[4], rb[4];
-  auto gload = [&](int kt) {
-    const int k = kt * kBK;
+  auto issue = [&](int kt) {
+    const int k = kt * BK;
     const bool s0 = k < K0;
     const int kk = s0 ? k : k - K0;
+    uint16_t* stage = &smem[kt % NS][0];
+    const uint16_t* abase = s0 ? p.a_base0() : p.a_base1();
+    const long lda = s0 ? p.lda0() : p.lda1();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      ra[j] = ga0[j] ? load8((s0 ? ga0[j] : ga1[j]) + kk) : zero8();
-      rb[j] = load8((s0 ? gb0[j] : gb1[j]) + kk);
+    for (int j = 0; j < NIA; ++j) {
+      // With two stages every wait is vmcnt(0), so instructions whose rows
+      // all lie past the tile's count can be skipped (with more stages the
+      // waits count a fixed number of loads per stage).
+      if (NS == 2 && RPI * (w + NW * j) >= mcount) continue;
+      const uint16_t* src;
+      if constexpr (GA) {
+        src = pa[j];
+      } else {
+        int row = RPI * (w + NW * j) + lr;
+        row = row < mcount ? row : 0;
+        src = abase + (long)(m0 + row) * lda + chunk8;
+      }
+      __builtin_amdgcn_global_load_lds((const void*)(src + kk),
+                                       (lds_void*)(stage + RPI * (w + NW * j) * BK), 16, 0, 0);
     }
-  };
-  auto sstore = [&](int st) {
+    const uint16_t* b = s0 ? pb0 : pb1;
+    const long sb = s0 ? sb0 : sb1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = lrow + 32 * j;
-      *reinterpret_cast<bf16x8*>(&sA[st][row * kLDK + lk]) = ra[j];
-      *reinterpret_cast<bf16x8*>(&sB[st][row * kLDK + lk]) = rb[j];
-    }
+    for (int j = 0; j < NIB; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(b + j * sb + kk),
+                                       (lds_void*)(stage + RPI * (w + NW * (NIA + j)) * BK), 16,
+                                       0, 0);
   };
 
-  const int wm = w >> 1, wn = w & 1;
-  const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  f32x4 acc[4][4];
+  const int wm = w / WGN, wn = w % WGN;
+  const int r16 = lane & 15, kq = lane >> 4;
+  f32x4 acc[TN][TM];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < TN; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < TM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue(s);
+
+  // Per k tile: wait for this tile's stage (own loads, then everyone's via
+  // the barrier, which also frees the stage written next), read every MFMA
+  // fragment of the tile from LDS, issue the DMA of tile kt + NS - 1 while
+  // those reads are in flight, then run the MFMAs.
+  constexpr int KS = BK / 32;
   for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+    if (kt + NS - 2 < nk)
+      wait_vmcnt<(NS - 2) * NI>();
+    else
+      wait_vmcnt<0>();
+    stage_barrier();
+    const uint16_t* st = &smem[kt % NS][0];
+    bf16x8 xf[KS][TM], wf[KS][TN];
 #pragma unroll
-    for (int ks = 0; ks < kBK / 32; ++ks) {
-      bf16x8 wf[4], xf[4];
+    for (int ks = 0; ks < KS; ++ks) {
+      const int q = ks * 4 + kq;
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        wf[g] = *reinterpret_cast<const bf16x8*>(
-            &sB[st][(wn * 64 + g * 16 + r16) * kLDK + ks * 32 + kq]);
+      for (int t = 0; t < TM; ++t) {
+        const int row = wm * (BM / 2) + t * 16 + r16;
+        if (wm * (BM / 2) + t * 16 < mcount)
+          xf[ks][t] = *reinterpret_cast<const bf16x8*>(st + row * BK + ((q ^ swz(row)) << 3));
+      }
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        xf[t] = *reinterpret_cast<const bf16x8*>(
-            &sA[st][(wm * 64 + t * 16 + r16) * kLDK + ks * 32 + kq]);
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[g][t] = mfma_bf16(wf[g], xf[t], acc[g][t]);
+      for (int gi = 0; gi < TN; ++gi) {
+        const int row = BM + wn * (BN / WGN) + gi * 16 + r16;
+        wf[ks][gi] = *reinterpret_cast<const bf16x8*>(st + row * BK + ((q ^ swz(row)) << 3));
+      }
     }
-    if (kt + 1 < nk) sstore(st ^ 1);
-    __syncthreads();
+    if (kt + NS - 1 < nk) issue(kt + NS - 1);
+    // token groups wholly past the tile's count are skipped (uniform branch)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+        if (wm * (BM / 2) + t * 16 < mcount)
+#pragma unroll
+          for (int gi = 0; gi < TN; ++gi) acc[gi][t] = mfma_bf16(wf[ks][gi], xf[ks][t], acc[gi][t]);
   }
 
   const int ncol = (lane >> 4) * 4;
 #pragma unroll
-  for (int g = 0; g < 4; ++g)
+  for (int gi = 0; gi < TN; ++gi)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int i = wm * 64 + t * 16 + r16;
-      if (i < mcount) p.store(e, m0 + i, n0 + wn * 64 + g * 16 + ncol, acc[g][t]);
+    for (int t = 0; t < TM; ++t) {
+      const int i = wm * (BM / 2) + t * 16 + r16;
+      if (i < mcount) p.store(e, m0 + i, n0 + wn * (BN / WGN) + gi * 16 + ncol, acc[gi][t]);
     }
 }
 
-template <class P>
-static hipError_t launch_dense(const P& p, int N, int T, hipStream_t s) {
-  const long grid = (long)((T + kBM - 1) / kBM) * (N / kBN);
+// Tile shapes used per problem (token rows x weight rows), from a sweep on
+// the full-shape prefill problems.  Expert GEMMs use 128-row token tiles:
+// with ~352 rows per expert at the prefill batch a 256-row tile would pad 45%
+// of the rows.
+constexpr int kExpBM = 128, kExpBN = 256, kExpBK = 64, kExpNS = 3;
+constexpr int kDenseBM = 256, kDenseBN = 256, kDenseBK = 64, kDenseNS = 2;
+constexpr int kWGN = 4;
+
+static long xcd_grid(long items) { return (items + kXcds - 1) / kXcds * kXcds; }
+
+template <class P, int BM, int BN, int BK, int NS>
+static hipError_t launch_dense(const P& p, int T, hipStream_t s) {
+  const long grid = xcd_grid((long)((T + BM - 1) / BM) * (p.N() / BN));
   if (grid <= 0) return hipSuccess;
-  tiled_gemm_kernel<P, false><<<grid, 256, 0, s>>>(p, T, nullptr, nullptr);
+  tiled_gemm_kernel<P, false, BM, BN, BK, NS, kWGN><<<grid, 128 * kWGN, 0, s>>>(p, T, nullptr,
+                                                                                nullptr);
   return hipGetLastError();
 }
 
-template <class P>
-static hipError_t launch_grouped(const P& p, int N, const Tile* tiles, const int* ntiles,
-                                 int max_tiles, hipStream_t s) {
-  const long grid = (long)max_tiles * (N / kBN);
+template <class P, int BM, int BN, int BK, int NS>
+static hipError_t launch_grouped(const P& p, const Tile* tiles, const int* ntiles, int max_tiles,
+                                 hipStream_t s) {
+  const long grid = xcd_grid((long)max_tiles * (p.N() / BN));
   if (grid <= 0) return hipSuccess;
-  tiled_gemm_kernel<P, true><<<grid, 256, 0, s>>>(p, 0, tiles, ntiles);
+  tiled_gemm_kernel<P, true, BM, BN, BK, NS, kWGN><<<grid, 128 * kWGN, 0, s>>>(p, 0, tiles,
+                                                                               ntiles);
   return hipGetLastError();
 }
 
-int tiled_block_m() { return kBM; }
-int tiled_block_n() { return kBN; }
+int tiled_block_m() { return kExpBM; }
+int tiled_block_n() { return 256; }
 
-hipError_t tiled_proj_in(const ProjIn& p, hipStream_t s) { return launch_dense(p, p.ncount, p.T, s); }
-hipError_t tiled_proj_out(const ProjOut& p, hipStream_t s) { return launch_dense(p, p.D, p.T, s); }
+hipError_t tiled_proj_in(const ProjIn& p, hipStream_t s) {
+  return launch_dense<ProjIn, kDenseBM, kDenseBN, kDenseBK, kDenseNS>(p, p.T, s);
+}
+hipError_t tiled_proj_out(const ProjOut& p, hipStream_t s) {
+  return launch_dense<ProjOut, kDenseBM, kDenseBN, kDenseBK, kDenseNS>(p, p.T, s);
+}
 hipError_t tiled_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, int max_tiles,
                         hipStream_t s) {
-  return launch_grouped(p, p.F, tiles, ntiles, max_tiles, s);
+  return launch_grouped<ExpUp, kExpBM, kExpBN, kExpBK, kExpNS>(p, tiles, ntiles, max_tiles, s);
 }
 hipError_t tiled_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles, int max_tiles,
                           hipStream_t s) {
-  return launch_grouped(p, p.R, tiles, ntiles, max_tiles, s);
+  return launch_grouped<ExpDown, kExpBM, kExpBN, kExpBK, kExpNS>(p, tiles, ntiles, max_tiles, s);
 }
 
 }  // namespace lmoe

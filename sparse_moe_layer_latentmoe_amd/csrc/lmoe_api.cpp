@@ -284,7 +284,7 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool tiled_ok = tiled_dims_ok(c);
   const bool dense_tiled =
-      tiled_ok && (c.path == LMOE_PATH_TILED || (c.path == LMOE_PATH_AUTO && T > 64));
+      tiled_ok && (c.path == LMOE_PATH_TILED || (c.path == LMOE_PATH_AUTO && T > 256));
   const bool expert_tiled =
       tiled_ok && (c.path == LMOE_PATH_TILED ||
                    (c.path == LMOE_PATH_AUTO && static_cast<long>(T) * K > 32L * E));

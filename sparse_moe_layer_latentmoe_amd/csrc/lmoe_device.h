@@ -74,9 +74,10 @@ __device__ __forceinline__ void store4_bf16_relu_sq(uint16_t* p, f32x4 v) {
 }
 
 // Work tile of the grouped expert GEMMs: rows [row0, row0 + nrows) of the
-// expert-sorted slot list all belong to `expert`.
+// expert-sorted slot list all belong to `expert`; the expert's tiles are
+// tiles [first, first + count) of the list.
 struct Tile {
-  int32_t expert, row0, nrows, pad;
+  int32_t expert, row0, nrows, first, count, pad0, pad1, pad2;
 };
 
 }  // namespace lmoe

@@ -15,28 +15,32 @@
 
 namespace lmoe {
 
-// logits[t][e] = sum_k z[t][k] * Wg[e][k].  Work-group: 16 experts x MT*16
-// tokens, the k range split over NW waves, partial sums added in LDS in a
-// fixed order.  Each lane loads 4 consecutive floats of its row per 16-wide
+// logits[t][e] = sum_k z[t][k] * Wg[e][k].  Work-group: RG*16 experts x
+// MT*16 tokens, the k range split over NW waves, partial sums added in LDS in
+// a fixed order.  Each lane loads 4 consecutive floats of its row per 16-wide
 // k step and feeds them to 4 MFMAs (16x16x4): MFMA j takes component j, so
-// lane group q = l/16 covers k = 4q + j -- the same for both operands.
-template <int NW, int MT>
+// lane group q = l/16 covers k = 4q + j -- the same for both operands.  Few
+// tokens: RG = 1 (many work-groups to stream the 4 MB gate); many tokens:
+// RG = 4, so each latent row loaded serves 64 experts.
+template <int NW, int MT, int RG>
 __global__ __launch_bounds__(NW * 64) void router_logits_kernel(const float* __restrict__ z,
                                                                 const float* __restrict__ wg,
                                                                 float* __restrict__ logits, int T,
                                                                 int E, int R) {
-  __shared__ f32x4 red[NW > 1 ? NW : 1][MT][64];
-  const int eblocks = E / 16;
+  constexpr int J = RG * MT;
+  __shared__ f32x4 red[NW > 1 ? NW : 1][J][64];
+  const int eblocks = E / (16 * RG);
   const int eb = blockIdx.x % eblocks;
   const int m0 = (blockIdx.x / eblocks) * (16 * MT);
-  const int e0 = eb * 16;
+  const int e0 = eb * 16 * RG;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, kq = (lane >> 4) * 4;
   const int kw = R / NW, kbeg = w * kw;
-  constexpr int KS = 64;  // k per pipeline stage (4 loads of 16 k)
+  constexpr int KS = 32;  // k per pipeline stage (2 loads of 16 k)
   const int nit = kw / KS;
 
   const float* brow = wg + (size_t)(e0 + r16) * R + kbeg + kq;
+  const long gstride = 16L * R;
   const float* arow[MT];
   bool av[MT];
 #pragma unroll
@@ -45,29 +49,35 @@ __global__ __launch_bounds__(NW * 64) void router_logits_kernel(const float* __r
     av[t] = m < T;
     arow[t] = av[t] ? z + (size_t)m * R + kbeg + kq : nullptr;
   }
-  f32x4 acc[MT];
+  f32x4 acc[RG][MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  f32x4 wA[4], xA[4][MT], wB[4], xB[4][MT];
-  auto load = [&](f32x4(&wf)[4], f32x4(&xf)[4][MT], int it) {
+  f32x4 wA[2][RG], xA[2][MT], wB[2][RG], xB[2][MT];
+  auto load = [&](f32x4(&wf)[2][RG], f32x4(&xf)[2][MT], int it) {
     const int k = it * KS;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      wf[u] = *reinterpret_cast<const f32x4*>(brow + k + u * 16);
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int g = 0; g < RG; ++g)
+        wf[u][g] = *reinterpret_cast<const f32x4*>(brow + g * gstride + k + u * 16);
 #pragma unroll
       for (int t = 0; t < MT; ++t)
         xf[u][t] = av[t] ? *reinterpret_cast<const f32x4*>(arow[t] + k + u * 16)
                          : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
-  auto compute = [&](const f32x4(&wf)[4], const f32x4(&xf)[4][MT]) {
+  auto compute = [&](const f32x4(&wf)[2][RG], const f32x4(&xf)[2][MT]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[t] = mfma_f32(wf[u][j], xf[u][t][j], acc[t]);
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+          for (int t = 0; t < MT; ++t) acc[g][t] = mfma_f32(wf[u][g][j], xf[u][t][j], acc[g][t]);
   };
   if (nit > 0) load(wA, xA, 0);
   for (int it = 0; it < nit; it += 2) {
@@ -81,18 +91,25 @@ __global__ __launch_bounds__(NW * 64) void router_logits_kernel(const float* __r
   const int ecol = e0 + (lane >> 4) * 4;
   if constexpr (NW == 1) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
-      if (av[t]) *reinterpret_cast<f32x4*>(logits + (size_t)(m0 + t * 16 + r16) * E + ecol) = acc[t];
+    for (int g = 0; g < RG; ++g)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        if (av[t])
+          *reinterpret_cast<f32x4*>(logits + (size_t)(m0 + t * 16 + r16) * E + ecol + g * 16) =
+              acc[g][t];
   } else {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) red[w][t][lane] = acc[t];
-    __syncthreads();
-    for (int t = w; t < MT; t += NW) {
-      f32x4 s = red[0][t][lane];
+    for (int g = 0; g < RG; ++g)
 #pragma unroll
-      for (int v = 1; v < NW; ++v) s += red[v][t][lane];
+      for (int t = 0; t < MT; ++t) red[w][g * MT + t][lane] = acc[g][t];
+    __syncthreads();
+    for (int jj = w; jj < J; jj += NW) {
+      f32x4 s = red[0][jj][lane];
+#pragma unroll
+      for (int v = 1; v < NW; ++v) s += red[v][jj][lane];
+      const int g = jj / MT, t = jj % MT;
       const int m = m0 + t * 16 + r16;
-      if (m < T) *reinterpret_cast<f32x4*>(logits + (size_t)m * E + ecol) = s;
+      if (m < T) *reinterpret_cast<f32x4*>(logits + (size_t)m * E + ecol + g * 16) = s;
     }
   }
 }
@@ -187,7 +204,8 @@ hipError_t router_logits(const float* z, const float* wg, float* logits, int T, 
                          hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int mt = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
-  const long grid = (long)((T + 16 * mt - 1) / (16 * mt)) * (E / 16);
+  const int rg = (T > 256 && E % 64 == 0) ? 4 : 1;
+  const long grid = (long)((T + 16 * mt - 1) / (16 * mt)) * (E / (16 * rg));
   int nw = 1;
   const int opts[4] = {1, 2, 4, 8};
   for (int i = 0; i < 4; ++i) {
@@ -195,10 +213,15 @@ hipError_t router_logits(const float* z, const float* wg, float* logits, int T, 
     nw = opts[i];
     if (grid * nw >= 2048) break;
   }
-#define LMOE_RL(NW_, MT_) \
-  router_logits_kernel<NW_, MT_><<<grid, NW_ * 64, 0, s>>>(z, wg, logits, T, E, R)
-#define LMOE_RL_MT(NW_) \
-  do { if (mt == 1) LMOE_RL(NW_, 1); else if (mt == 2) LMOE_RL(NW_, 2); else LMOE_RL(NW_, 4); } while (0)
+#define LMOE_RL(NW_, MT_, RG_) \
+  router_logits_kernel<NW_, MT_, RG_><<<grid, NW_ * 64, 0, s>>>(z, wg, logits, T, E, R)
+#define LMOE_RL_MT(NW_)                 \
+  do {                                  \
+    if (rg == 4) LMOE_RL(NW_, 4, 4);    \
+    else if (mt == 1) LMOE_RL(NW_, 1, 1); \
+    else if (mt == 2) LMOE_RL(NW_, 2, 1); \
+    else LMOE_RL(NW_, 4, 1);            \
+  } while (0)
   switch (nw) {
     case 1: LMOE_RL_MT(1); break;
     case 2: LMOE_RL_MT(2); break;
