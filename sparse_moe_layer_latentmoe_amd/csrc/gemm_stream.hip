@@ -4,33 +4,52 @@
 // from HBM once; the page's own accounting puts decode on weight I/O and
 // prefill on compute ("Nemotron 3 架构解读", the decode/prefill discussion).
 // So this kernel is built around one thing: every weight byte is read
-// exactly once, with many 16-byte loads in flight per wave, and turned into
-// MFMA operands straight from registers (no LDS staging of weights).
+// exactly once, as whole cache lines, with many loads in flight per wave.
 //
-// Work-group = NW waves on one block of RG*16 weight rows (RG MFMA row
-// groups of 16) and MT*16 token rows.  The k range is split evenly over the
-// NW waves (so many waves stream disjoint parts of the same rows); each wave
-// keeps a double-buffered register pipeline of U k steps of (RG weight + MT
-// activation) fragments, then the waves' partial sums are added in LDS in a
-// fixed order (deterministic) and the problem's epilogue stores.
+// Work-group = NW waves on one block of RG*16 weight rows and MT*16 token
+// rows; the k range is split evenly over the waves, whose partial sums are
+// added in LDS in a fixed order (deterministic).  Weights are the MFMA A
+// operand (rows = output columns), activations the B operand (columns =
+// tokens), so each lane ends with four consecutive output columns of one
+// token.
 //
-// Weights are the MFMA A operand (rows = output columns n), activations the
-// B operand (columns = tokens), so each lane ends with four consecutive
-// output columns of one token: an 8- or 16-byte store.
+// Weight loads: one wave instruction reads 8 rows x 128 bytes (64 k), i.e.
+// whole cache lines, with the non-temporal hint; two such loads (rows 0-7
+// and 8-15 of a row group) hold the two 16x32 MFMA fragments of that 64-k
+// chunk, and ds_bpermute moves each 16-byte piece to the lane the MFMA
+// layout wants (lane (r, q) of step s takes row r, k chunk 4s + q).
+// Measured on MI355X (decode expert GEMMs, ~400 experts): 6.9 TB/s, against
+// 6.2-6.4 TB/s for loading the fragments directly (16 rows x 64 bytes per
+// instruction, where the nt hint makes it worse, not better).
 #include "gemm_problems.h"
 #include "kernels.h"
 
 namespace lmoe {
 
-// NT: load weights with the non-temporal hint (kept for measurement; the
-// launch shapes below use plain loads).
-template <class P, bool GROUPED, int NW, int MT, int kRG, int kU, bool NT>
+// Fragment for MFMA step s from the two 8-row loads a (rows 0-7) and b
+// (rows 8-15): the lane reads byte offset src4 of the other lanes' data and
+// keeps a's value for rows 0-7, b's for rows 8-15.
+__device__ __forceinline__ bf16x8 permute_frag(const bf16x8& a, const bf16x8& b, int src4,
+                                               bool lo) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const i32x4 ai = __builtin_bit_cast(i32x4, a), bi = __builtin_bit_cast(i32x4, b);
+  i32x4 r;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const int va = __builtin_amdgcn_ds_bpermute(src4, ai[d]);
+    const int vb = __builtin_amdgcn_ds_bpermute(src4, bi[d]);
+    r[d] = lo ? va : vb;
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+template <class P, bool GROUPED, int NW, int MT, int RG, int U>
 __global__ __launch_bounds__(NW * 64) void stream_gemm_kernel(P p, int mrows, const Tile* tiles,
                                                               const int* ntiles) {
-  constexpr int J = kRG * MT;
+  constexpr int J = RG * MT;
   __shared__ f32x4 red[NW > 1 ? NW : 1][J][64];
 
-  const int nblocks = p.N() / (16 * kRG);
+  const int nblocks = p.N() / (16 * RG);
   int nb, tm;
   if (GROUPED) {
     nb = blockIdx.x % nblocks;
@@ -56,85 +75,105 @@ __global__ __launch_bounds__(NW * 64) void stream_gemm_kernel(P p, int mrows, co
     m0 = tm * (16 * MT);
     mcount = min(16 * MT, mrows - m0);
   }
-  const int n0 = nb * (16 * kRG);
+  const int n0 = nb * (16 * RG);
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int r16 = lane & 15;
-  const int kq = (lane >> 4) * 8;
+  const int kq = lane >> 4;
   const int K = p.K(), K0 = p.K0();
   const int kw = K / NW;
   const int kbeg = w * kw;
-  const int nit = kw / (32 * kU);
+  const int nit = kw / (64 * U);
 
-  const uint16_t* b0[kRG];
-  const uint16_t* b1[kRG];
+  // Weight load layout: lane -> row lane / 8 (+8 for the second load), k
+  // chunk lane % 8.  Pointers for both k segments (segment 1 only exists for
+  // the K-concatenated output projection).
+  const int lrow = lane >> 3, lch = (lane & 7) * 8;
+  const uint16_t* wa0[RG];
+  const uint16_t* wb0[RG];
+  const uint16_t* wa1[RG];
+  const uint16_t* wb1[RG];
 #pragma unroll
-  for (int g = 0; g < kRG; ++g) {
-    b0[g] = p.b_row0(e, n0 + g * 16 + r16) + kq;
-    const uint16_t* q = p.b_row1(e, n0 + g * 16 + r16);
-    b1[g] = q ? q + kq : nullptr;
+  for (int g = 0; g < RG; ++g) {
+    wa0[g] = p.b_row0(e, n0 + g * 16 + lrow) + lch;
+    wb0[g] = p.b_row0(e, n0 + g * 16 + 8 + lrow) + lch;
+    const uint16_t* qa = p.b_row1(e, n0 + g * 16 + lrow);
+    const uint16_t* qb = p.b_row1(e, n0 + g * 16 + 8 + lrow);
+    wa1[g] = qa ? qa + lch : nullptr;
+    wb1[g] = qb ? qb + lch : nullptr;
   }
-  const uint16_t* a0[MT];
-  const uint16_t* a1[MT];
-  bool av[MT];
+  // Activation rows past the tile's count read the tile's first row (their
+  // outputs are never stored).
+  const uint16_t* x0[MT];
+  const uint16_t* x1[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int i = t * 16 + r16;
-    av[t] = i < mcount;
-    a0[t] = av[t] ? p.a_row0(m0 + i) + kq : nullptr;
-    const uint16_t* q = av[t] ? p.a_row1(m0 + i) : nullptr;
-    a1[t] = q ? q + kq : nullptr;
+    const int row = m0 + (i < mcount ? i : 0);
+    x0[t] = p.a_row0(row) + kq * 8;
+    const uint16_t* q = p.a_row1(row);
+    x1[t] = q ? q + kq * 8 : nullptr;
   }
+  const int src0 = (((r16 & 7) << 3) | kq) * 4;
+  const int src1 = (((r16 & 7) << 3) | (4 + kq)) * 4;
+  const bool lo = r16 < 8;
 
-  f32x4 acc[kRG][MT];
+  f32x4 acc[RG][MT];
 #pragma unroll
-  for (int g = 0; g < kRG; ++g)
+  for (int g = 0; g < RG; ++g)
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  bf16x8 wA[kU][kRG], xA[kU][MT], wB[kU][kRG], xB[kU][MT];
-
-  auto load = [&](bf16x8(&wf)[kU][kRG], bf16x8(&xf)[kU][MT], int it) {
-    const int k = kbeg + it * (32 * kU);
+  bf16x8 LA[U][RG][2], XA[U][MT][2], LB[U][RG][2], XB[U][MT][2];
+  auto load = [&](bf16x8(&L)[U][RG][2], bf16x8(&X)[U][MT][2], int it) {
+    const int k = kbeg + it * (64 * U);
     const bool s0 = k < K0;
     const int kk = s0 ? k : k - K0;
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int g = 0; g < kRG; ++g) {
-        const uint16_t* q = (s0 ? b0[g] : b1[g]) + kk + u * 32;
-        wf[u][g] = NT ? load8_stream(q) : load8(q);
+      for (int g = 0; g < RG; ++g) {
+        L[u][g][0] = load8_stream((s0 ? wa0[g] : wa1[g]) + kk + u * 64);
+        L[u][g][1] = load8_stream((s0 ? wb0[g] : wb1[g]) + kk + u * 64);
       }
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-        xf[u][t] = av[t] ? load8((s0 ? a0[t] : a1[t]) + kk + u * 32) : zero8();
+      for (int t = 0; t < MT; ++t) {
+        const uint16_t* x = (s0 ? x0[t] : x1[t]) + kk + u * 64;
+        X[u][t][0] = load8(x);
+        X[u][t][1] = load8(x + 32);
+      }
+    }
   };
-  auto compute = [&](const bf16x8(&wf)[kU][kRG], const bf16x8(&xf)[kU][MT]) {
+  auto compute = [&](const bf16x8(&L)[U][RG][2], const bf16x8(&X)[U][MT][2]) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int g = 0; g < kRG; ++g)
+      for (int g = 0; g < RG; ++g) {
+        const bf16x8 f0 = permute_frag(L[u][g][0], L[u][g][1], src0, lo);
+        const bf16x8 f1 = permute_frag(L[u][g][0], L[u][g][1], src1, lo);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) acc[g][t] = mfma_bf16(wf[u][g], xf[u][t], acc[g][t]);
+        for (int t = 0; t < MT; ++t) {
+          acc[g][t] = mfma_bf16(f0, X[u][t][0], acc[g][t]);
+          acc[g][t] = mfma_bf16(f1, X[u][t][1], acc[g][t]);
+        }
+      }
   };
 
-  if (nit > 0) load(wA, xA, 0);
+  if (nit > 0) load(LA, XA, 0);
   for (int it = 0; it < nit; it += 2) {
-    if (it + 1 < nit) load(wB, xB, it + 1);
-    compute(wA, xA);
+    if (it + 1 < nit) load(LB, XB, it + 1);
+    compute(LA, XA);
     if (it + 1 < nit) {
-      if (it + 2 < nit) load(wA, xA, it + 2);
-      compute(wB, xB);
+      if (it + 2 < nit) load(LA, XA, it + 2);
+      compute(LB, XB);
     }
   }
 
   const int ncol = (lane >> 4) * 4;
   if constexpr (NW == 1) {
 #pragma unroll
-    for (int g = 0; g < kRG; ++g)
+    for (int g = 0; g < RG; ++g)
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         const int i = t * 16 + r16;
@@ -142,41 +181,38 @@ __global__ __launch_bounds__(NW * 64) void stream_gemm_kernel(P p, int mrows, co
       }
   } else {
 #pragma unroll
-    for (int g = 0; g < kRG; ++g)
+    for (int g = 0; g < RG; ++g)
 #pragma unroll
       for (int t = 0; t < MT; ++t) red[w][g * MT + t][lane] = acc[g][t];
     __syncthreads();
     for (int j = w; j < J; j += NW) {
-      f32x4 s = red[0][j][lane];
+      f32x4 sm = red[0][j][lane];
 #pragma unroll
-      for (int v = 1; v < NW; ++v) s += red[v][j][lane];
+      for (int v = 1; v < NW; ++v) sm += red[v][j][lane];
       const int g = j / MT, t = j % MT;
       const int i = t * 16 + r16;
-      if (i < mcount) p.store(e, m0 + i, n0 + g * 16 + ncol, s);
+      if (i < mcount) p.store(e, m0 + i, n0 + g * 16 + ncol, sm);
     }
   }
 }
 
-// Launch shapes.  Measured on MI355X with the full-shape decode problems
-// (T = 32, ~400 touched experts): plain loads beat the non-temporal hint for
-// this access pattern (each wave instruction touches half of 16 cache lines,
-// and the other half is wanted by the next instruction), and the shapes
-// below were the fastest of a sweep over waves/work-group, row groups and
-// pipeline depth.  A shape is used only if it divides the problem; the
-// chain ends in one that always does (dimensions are multiples of 64).
+// Launch shapes (waves per work-group, row groups, 64-k chunks per pipeline
+// stage), from a sweep on the full-shape decode problems.  A shape is used
+// only if it divides the problem; the chain ends in one that always does
+// (dimensions are multiples of 64).
 struct Shape {
   int nw, rg, u;
 };
 
 static bool fits(const Shape& c, int N, int K, int K0) {
-  return K % (c.nw * 32 * c.u) == 0 && K0 % (32 * c.u) == 0 && N % (16 * c.rg) == 0;
+  return K % (c.nw * 64 * c.u) == 0 && K0 % (64 * c.u) == 0 && N % (16 * c.rg) == 0;
 }
 
 static Shape pick(const Shape& pref, int N, int K, int K0) {
-  const Shape chain[] = {pref, {4, 2, 2}, {2, 2, 2}, {1, 2, 2}, {1, 1, 2}};
+  const Shape chain[] = {pref, {4, 4, 1}, {4, 2, 1}, {2, 2, 1}, {1, 2, 1}, {1, 1, 1}};
   for (const Shape& c : chain)
     if (fits(c, N, K, K0)) return c;
-  return {1, 1, 2};
+  return {1, 1, 1};
 }
 
 template <class P, bool GROUPED, int MT>
@@ -185,19 +221,19 @@ static hipError_t launch_shape(const P& p, const Shape& c, long mtiles, int mrow
   const long nblocks = p.N() / (16 * c.rg);
   const long grid = GROUPED ? mtiles * nblocks : 8 * mtiles * ((nblocks + 7) / 8);
   if (grid <= 0) return hipSuccess;
-#define LMOE_SG(NW_, RG_, U_)                                                              \
-  if (c.nw == NW_ && c.rg == RG_ && c.u == U_) {                                           \
-    stream_gemm_kernel<P, GROUPED, NW_, MT, RG_, U_, false>                                \
-        <<<grid, NW_ * 64, 0, s>>>(p, mrows, tiles, ntiles);                               \
-    return hipGetLastError();                                                              \
+#define LMOE_SG(NW_, RG_, U_)                                                      \
+  if (c.nw == NW_ && c.rg == RG_ && c.u == U_) {                                   \
+    stream_gemm_kernel<P, GROUPED, NW_, MT, RG_, U_>                               \
+        <<<grid, NW_ * 64, 0, s>>>(p, mrows, tiles, ntiles);                       \
+    return hipGetLastError();                                                      \
   }
+  LMOE_SG(4, 4, 1)
   LMOE_SG(4, 4, 2)
-  LMOE_SG(4, 4, 4)
-  LMOE_SG(8, 2, 4)
+  LMOE_SG(4, 2, 1)
   LMOE_SG(4, 2, 2)
-  LMOE_SG(2, 2, 2)
-  LMOE_SG(1, 2, 2)
-  LMOE_SG(1, 1, 2)
+  LMOE_SG(2, 2, 1)
+  LMOE_SG(1, 2, 1)
+  LMOE_SG(1, 1, 1)
 #undef LMOE_SG
   return hipErrorInvalidConfiguration;
 }
@@ -222,18 +258,18 @@ static hipError_t launch_grouped(const P& p, const Shape& pref, const Tile* tile
 }
 
 hipError_t stream_proj_in(const ProjIn& p, hipStream_t s) {
-  return launch_dense(p, Shape{4, 4, 2}, p.T, s);
+  return launch_dense(p, Shape{4, 4, 1}, p.T, s);
 }
 hipError_t stream_proj_out(const ProjOut& p, hipStream_t s) {
-  return launch_dense(p, Shape{4, 2, 2}, p.T, s);
+  return launch_dense(p, Shape{4, 4, 1}, p.T, s);
 }
 hipError_t stream_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, int max_tiles,
                          hipStream_t s) {
-  return launch_grouped(p, Shape{4, 4, 4}, tiles, ntiles, max_tiles, s);
+  return launch_grouped(p, Shape{4, 4, 1}, tiles, ntiles, max_tiles, s);
 }
 hipError_t stream_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles, int max_tiles,
                            hipStream_t s) {
-  return launch_grouped(p, Shape{8, 2, 4}, tiles, ntiles, max_tiles, s);
+  return launch_grouped(p, Shape{4, 4, 1}, tiles, ntiles, max_tiles, s);
 }
 
 }  // namespace lmoe

@@ -238,10 +238,12 @@ __global__ __launch_bounds__(128 * WGN) void tiled_gemm_kernel(P p, int mrows, c
 }
 
 // Tile shapes used per problem (token rows x weight rows), from a sweep on
-// the full-shape prefill problems.  Expert GEMMs use 128-row token tiles:
-// with ~352 rows per expert at the prefill batch a 256-row tile would pad 45%
-// of the rows.
-constexpr int kExpBM = 128, kExpBN = 256, kExpBK = 64, kExpNS = 3;
+// the full-shape prefill problems.  Expert GEMMs use 128-row token tiles
+// (with ~352 rows per expert at the prefill batch a 256-row tile would pad
+// 45% of the rows) and 512 weight rows where N allows (fewer bytes moved per
+// flop: measured, the vector-memory data path, not the MFMAs, limits these
+// GEMMs), else 256.
+constexpr int kExpBM = 128, kExpBK = 64;
 constexpr int kDenseBM = 256, kDenseBN = 256, kDenseBK = 64, kDenseNS = 2;
 constexpr int kWGN = 4;
 
@@ -275,13 +277,21 @@ hipError_t tiled_proj_in(const ProjIn& p, hipStream_t s) {
 hipError_t tiled_proj_out(const ProjOut& p, hipStream_t s) {
   return launch_dense<ProjOut, kDenseBM, kDenseBN, kDenseBK, kDenseNS>(p, p.T, s);
 }
+template <class P>
+static hipError_t launch_expert(const P& p, const Tile* tiles, const int* ntiles, int max_tiles,
+                                hipStream_t s) {
+  if (p.N() % 512 == 0)
+    return launch_grouped<P, kExpBM, 512, kExpBK, 2>(p, tiles, ntiles, max_tiles, s);
+  return launch_grouped<P, kExpBM, 256, kExpBK, 3>(p, tiles, ntiles, max_tiles, s);
+}
+
 hipError_t tiled_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, int max_tiles,
                         hipStream_t s) {
-  return launch_grouped<ExpUp, kExpBM, kExpBN, kExpBK, kExpNS>(p, tiles, ntiles, max_tiles, s);
+  return launch_expert(p, tiles, ntiles, max_tiles, s);
 }
 hipError_t tiled_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles, int max_tiles,
                           hipStream_t s) {
-  return launch_grouped<ExpDown, kExpBM, kExpBN, kExpBK, kExpNS>(p, tiles, ntiles, max_tiles, s);
+  return launch_expert(p, tiles, ntiles, max_tiles, s);
 }
 
 }  // namespace lmoe
