@@ -61,6 +61,35 @@ def stage_work(sh, T, U):
     return b, f
 
 
+def source_sha256():
+    """Hash of the HIP sources, to tell whether stored counter data still
+    describes the kernels being run."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "sparse_moe_layer_latentmoe_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per launch of `stage` (calibrated FETCH_SIZE + WRITE_SIZE
+    from the rocprofv3 counter runs kept under profiles/), or None when no
+    such measurement exists for this workload or the kernels have changed
+    since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_T32.json")
+    if workload != "decode" or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    st = d.get("stages", {}).get(stage)
+    if st is None or d.get("source_sha256") != source_sha256():
+        return None
+    return int(st["fetch_bytes"] + st["write_bytes"])
+
+
 def bf16_flops(sh, T):
     D, R, K, F, S = (sh.hidden_size, sh.moe_latent_size, sh.num_experts_per_tok,
                      sh.moe_intermediate_size, sh.moe_shared_expert_intermediate_size)
@@ -148,7 +177,8 @@ def main():
     if hbm:
         ach = sb[dom] / (stage_ms[dom] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(args.workload, dom), "kernel": dom,
                 "algorithmic_bytes_per_launch": sb[dom], "avg_launch_ms": round(stage_ms[dom], 5)}
         layer_bytes = sum(sb.values())
         layer_ach = layer_bytes / (ms * 1e-3) / 1e9
