@@ -33,8 +33,9 @@
  *    the same time.
  *  - the first lmoe_forward on a handle creates one auxiliary HIP stream
  *    (non-blocking, default priority) and two events, used to run the shared
- *    expert's up projection concurrently with the router (forked from and
- *    joined back into `stream`); lmoe_destroy releases them.
+ *    expert's up projection concurrently with the router (forked from
+ *    `stream` after the latent projection and joined back before the output
+ *    projection); lmoe_destroy releases them.
  */
 #ifndef LMOE_H
 #define LMOE_H
@@ -130,7 +131,7 @@ const char *lmoe_status_string(lmoe_status s);
 /* Number of timed stages of lmoe_forward and the name of stage i.  Stages
  * 0..7 run back to back on the forward's stream (the last one, proj_out,
  * includes the wait for the auxiliary stream); stage 8 ("shared_up") is
- * timed on the auxiliary stream and overlaps stages 0..6. */
+ * timed on the auxiliary stream and overlaps stages 1..6. */
 int32_t lmoe_num_stages(void);
 const char *lmoe_stage_name(int32_t i);
 

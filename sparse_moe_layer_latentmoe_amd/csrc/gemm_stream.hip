@@ -227,8 +227,10 @@ static hipError_t launch_shape(const P& p, const Shape& c, long mtiles, int mrow
         <<<grid, NW_ * 64, 0, s>>>(p, mrows, tiles, ntiles);                       \
     return hipGetLastError();                                                      \
   }
+  LMOE_SG(8, 1, 2)
+  LMOE_SG(8, 2, 1)
+  LMOE_SG(8, 4, 1)
   LMOE_SG(4, 4, 1)
-  LMOE_SG(4, 4, 2)
   LMOE_SG(4, 2, 1)
   LMOE_SG(4, 2, 2)
   LMOE_SG(2, 2, 1)
@@ -258,10 +260,11 @@ static hipError_t launch_grouped(const P& p, const Shape& pref, const Tile* tile
 }
 
 hipError_t stream_proj_in(const ProjIn& p, hipStream_t s) {
-  return launch_dense(p, Shape{4, 4, 1}, p.T, s);
+  // the latent part (few rows) wants many short waves; the shared part wider blocks
+  return launch_dense(p, p.N() <= 4096 ? Shape{8, 1, 2} : Shape{8, 4, 1}, p.T, s);
 }
 hipError_t stream_proj_out(const ProjOut& p, hipStream_t s) {
-  return launch_dense(p, Shape{4, 4, 1}, p.T, s);
+  return launch_dense(p, Shape{8, 2, 1}, p.T, s);
 }
 hipError_t stream_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, int max_tiles,
                          hipStream_t s) {

@@ -11,8 +11,8 @@
 //   expert_down    H Wdn[e]^T                                  (Step 6)
 //   combine        r = sum_k w O                               (Step 6 index_add_)
 //   proj_out       y = r W2^T + Hs Wsd^T                       (Step 7)
-// and, forked onto the handle's auxiliary stream right after the caller's
-// prior work and joined before proj_out (the shared expert only needs x):
+// and, forked onto the handle's auxiliary stream after proj_latent and
+// joined before proj_out (the shared expert only needs x):
 //   shared_up      x -> relu(x Wsu^T)^2                        (Step 7)
 // The router/dispatch chain is latency-bound and leaves HBM idle; the
 // shared expert's weight stream fills that time.
@@ -324,7 +324,13 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   };
   auto ok = [](hipError_t e) { return e == hipSuccess; };
 
-  // fork: the shared expert's up projection on the auxiliary stream
+  if (!mark()) return LMOE_ERR_HIP;
+  ProjIn platent{x, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, 0, R};
+  if (!ok(dense_tiled ? tiled_proj_in(platent, s) : stream_proj_in(platent, s)))
+    return LMOE_ERR_HIP;
+  // fork after the latent (the router's input) so that it runs alone: the
+  // shared expert's up projection then streams on the auxiliary stream while
+  // the latency-bound router and dispatch kernels run
   if (!ok(hipEventRecord(h->fork, s)) || !ok(hipStreamWaitEvent(h->aux, h->fork, 0)))
     return LMOE_ERR_HIP;
   if (ev && !ok(hipEventRecord(ev[kMainStages + 1], h->aux))) return LMOE_ERR_HIP;
@@ -333,11 +339,6 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
     return LMOE_ERR_HIP;
   if (ev && !ok(hipEventRecord(ev[kMainStages + 2], h->aux))) return LMOE_ERR_HIP;
   if (!ok(hipEventRecord(h->join, h->aux))) return LMOE_ERR_HIP;
-
-  if (!mark()) return LMOE_ERR_HIP;
-  ProjIn platent{x, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, 0, R};
-  if (!ok(dense_tiled ? tiled_proj_in(platent, s) : stream_proj_in(platent, s)))
-    return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
   if (!ok(router_logits(z32, h->w.router, logits, T, E, R, s))) return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
