@@ -32,11 +32,18 @@ hipError_t tiled_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles
 int tiled_block_m();
 int tiled_block_n();
 
-// Router: fp32 logits [T, E], then per token sigmoid / bias / top-K / weights.
+// Router: fp32 logits, then per token sigmoid / bias / top-K / weights.  The
+// logits GEMM may split k over router_splits(T, E, R) partial [T, E] arrays
+// (logits must hold that many); router_select adds them in split order.
+// Splitting happens only for T <= router_split_max_tokens(), into at most
+// router_max_splits() parts.
+constexpr int router_max_splits() { return 8; }
+constexpr int router_split_max_tokens() { return 1024; }
+int router_splits(int T, int E, int R);
 hipError_t router_logits(const float* z, const float* wg, float* logits, int T, int E, int R,
                          hipStream_t s);
-hipError_t router_select(const float* logits, const float* bias, int T, int E, int K, float rho,
-                         int32_t* idx, float* w, hipStream_t s);
+hipError_t router_select(const float* logits, const float* bias, int T, int E, int R, int K,
+                         float rho, int32_t* idx, float* w, hipStream_t s);
 
 // Grouping by expert: counts[E], offsets[E+1], rows_tok[T*K], inv[T*K] and
 // the tile list (tiles of at most tile_m rows) with its length in *ntiles.

@@ -100,7 +100,9 @@ Layout make_layout(const lmoe_config& c) {
   L.z32 = take(T * R * 4);
   L.z16 = take(T * R * 2);
   L.hs = take(T * S * 2);
-  L.logits = take(T * E * 4);
+  L.logits = take(std::max(T, std::min<size_t>(T, router_split_max_tokens()) *
+                                  static_cast<size_t>(router_max_splits())) *
+                  E * 4);
   L.idx = take(slots * 4);
   L.tw = take(slots * 4);
   L.counts = take(E * 4);
@@ -253,8 +255,9 @@ lmoe_status lmoe_route(lmoe_handle* h, const float* z_f32, int32_t T, int32_t* t
   if (router_logits(z_f32, h->w.router, logits, T, c.n_routed_experts, c.moe_latent_size, s) !=
       hipSuccess)
     return LMOE_ERR_HIP;
-  if (router_select(logits, h->w.router_bias, T, c.n_routed_experts, c.num_experts_per_tok,
-                    c.routed_scaling_factor, topk_idx, topk_w, s) != hipSuccess)
+  if (router_select(logits, h->w.router_bias, T, c.n_routed_experts, c.moe_latent_size,
+                    c.num_experts_per_tok, c.routed_scaling_factor, topk_idx, topk_w,
+                    s) != hipSuccess)
     return LMOE_ERR_HIP;
   return LMOE_OK;
 }
@@ -342,7 +345,7 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   if (!mark()) return LMOE_ERR_HIP;
   if (!ok(router_logits(z32, h->w.router, logits, T, E, R, s))) return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
-  if (!ok(router_select(logits, h->w.router_bias, T, E, K, c.routed_scaling_factor, idx, tw, s)))
+  if (!ok(router_select(logits, h->w.router_bias, T, E, R, K, c.routed_scaling_factor, idx, tw, s)))
     return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
   if (!ok(dispatch(idx, T, K, E, blockcnt, counts, offsets, rows_tok, inv, tiles, ntiles, tile_m,

@@ -10,6 +10,9 @@
 //
 // Two kernels: the logits GEMM (fp32 MFMA, weight-streaming layout like the
 // bf16 streaming GEMM) and one wavefront per token for everything after it.
+// With few tokens the GEMM also splits k over work-groups (the 4 MB gate is
+// otherwise streamed by a few dozen work-groups); the selection kernel adds
+// the split partial logits in a fixed order.
 #include "kernels.h"
 #include "lmoe_device.h"
 
@@ -22,20 +25,27 @@ namespace lmoe {
 // lane group q = l/16 covers k = 4q + j -- the same for both operands.  Few
 // tokens: RG = 1 (many work-groups to stream the 4 MB gate); many tokens:
 // RG = 4, so each latent row loaded serves 64 experts.
+// Work-group b: k split b / (mtiles * eblocks) of `nsplit` (each R / nsplit
+// long), writing partial logits to logits + split * T * E.
 template <int NW, int MT, int RG>
 __global__ __launch_bounds__(NW * 64) void router_logits_kernel(const float* __restrict__ z,
                                                                 const float* __restrict__ wg,
                                                                 float* __restrict__ logits, int T,
-                                                                int E, int R) {
+                                                                int E, int R, int nsplit) {
   constexpr int J = RG * MT;
   __shared__ f32x4 red[NW > 1 ? NW : 1][J][64];
   const int eblocks = E / (16 * RG);
-  const int eb = blockIdx.x % eblocks;
-  const int m0 = (blockIdx.x / eblocks) * (16 * MT);
+  const int mtiles = (T + 16 * MT - 1) / (16 * MT);
+  const int split = blockIdx.x / (eblocks * mtiles);
+  const int bid = blockIdx.x % (eblocks * mtiles);
+  const int eb = bid % eblocks;
+  const int m0 = (bid / eblocks) * (16 * MT);
   const int e0 = eb * 16 * RG;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, kq = (lane >> 4) * 4;
-  const int kw = R / NW, kbeg = w * kw;
+  const int rs = R / nsplit;
+  const int kw = rs / NW, kbeg = split * rs + w * kw;
+  logits += (size_t)split * T * E;
   constexpr int KS = 32;  // k per pipeline stage (2 loads of 16 k)
   const int nit = kw / KS;
 
@@ -122,23 +132,18 @@ __device__ __forceinline__ uint32_t ordered_bits(float b) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
 // One wavefront per token.  Expert e = 64 j + lane lives in slot j of lane
-// `lane`.  Key = (ordered biased score, ~expert id): the largest key is the
-// highest biased score, equal scores going to the lower expert id.  K rounds
-// of a wave-wide maximum pick the K experts; their output order is
-// ascending expert id, the renormalising sum is a plain float32 sum in that
-// order, then w = (s / (sum + 1e-20)) * rho.
+// `lane`; its key is the ordered bit pattern of its biased score (0 for slots
+// past E, below every finite score).  The K-th largest key v is built bit by
+// bit from the top: a candidate stays if at least K keys reach it, counted
+// with one ballot per slot (no cross-lane data movement).  The selected set
+// is every key above v plus the lowest-id experts whose key equals v (equal
+// scores go to the lower expert id).  Output order is ascending expert id,
+// the renormalising sum is a plain float32 sum in that order, then
+// w = (s / (sum + 1e-20)) * rho.
 template <int NJ>
 __global__ __launch_bounds__(256) void router_select_kernel(const float* __restrict__ logits,
+                                                           int nsplit,
                                                            const float* __restrict__ bias, int T,
                                                            int E, int K, float rho,
                                                            int32_t* __restrict__ idx_out,
@@ -147,38 +152,60 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
   if (t >= T) return;
+  const size_t pstride = (size_t)T * E;
+  // logit = partial 0 + partial 1 + ... (split order); all slots' loads of a
+  // batch of partials are issued before any is added
+  const float* lp = logits + (size_t)t * E + lane;
+  float l[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) l[j] = (j * 64 + lane < E) ? lp[j * 64] : 0.f;
+  for (int q0 = 1; q0 < nsplit; q0 += 4) {
+    float pv[4][NJ];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        pv[q][j] = (q0 + q < nsplit && j * 64 + lane < E) ? lp[(q0 + q) * pstride + j * 64] : 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q0 + q < nsplit)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) l[j] += pv[q][j];
+  }
   float s[NJ];
-  uint64_t key[NJ];
+  uint32_t key[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = j * 64 + lane;
     if (e < E) {
-      const float l = logits[(size_t)t * E + e];
-      s[j] = 1.0f / (1.0f + expf(-l));
-      const float b = s[j] + bias[e];
-      key[j] = (static_cast<uint64_t>(ordered_bits(b)) << 32) | (0xFFFFFFFFu - (uint32_t)e);
+      s[j] = 1.0f / (1.0f + expf(-l[j]));
+      key[j] = ordered_bits(s[j] + bias[e]);
     } else {
       s[j] = 0.f;
-      key[j] = 0;
+      key[j] = 0u;
     }
   }
-  uint32_t sel = 0;
-  for (int r = 0; r < K; ++r) {
-    uint64_t best = 0;
+  uint32_t v = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = v | (1u << bit);
+    int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      if (!((sel >> j) & 1u) && key[j] > best) best = key[j];
-    const uint64_t wbest = wave_max_u64(best);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      if (key[j] == wbest) sel |= 1u << j;
+    for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(key[j] >= c));
+    if (cnt >= K) v = c;
   }
-  // Position of each selected expert in ascending id order.
-  int base = 0;
+  int above = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) above += __popcll(__ballot(key[j] > v));
+  int room = K - above;  // experts with key == v still to take, lowest ids first
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int base = 0;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const bool on = (sel >> j) & 1u;
+    const uint64_t eq = __ballot(key[j] == v);
+    bool on = key[j] > v;
+    if (key[j] == v && __popcll(eq & below) < room) on = true;
+    const int took = __popcll(eq);
+    room -= took < room ? took : room;
     const uint64_t m = __ballot(on);
     if (on) {
       const int pos = base + __popcll(m & below);
@@ -200,21 +227,44 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
   if (lane < K) w_out[(size_t)t * K + lane] = (ssel[wv][lane] / denom) * rho;
 }
 
+// Launch geometry of the logits GEMM for T tokens.
+struct RouterGeom {
+  int mt, rg, nsplit, nw;
+  long grid;
+};
+
+static RouterGeom router_geom(int T, int E, int R) {
+  RouterGeom g;
+  g.mt = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
+  g.rg = (T > 256 && E % 64 == 0) ? 4 : 1;
+  const long base = (long)((T + 16 * g.mt - 1) / (16 * g.mt)) * (E / (16 * g.rg));
+  // split k until about 512 work-groups, keeping each split a multiple of 64
+  g.nsplit = 1;
+  while (g.nsplit < router_max_splits() && base * g.nsplit * 2 <= 512 &&
+         R % (g.nsplit * 2 * 64) == 0 && T <= router_split_max_tokens())
+    g.nsplit *= 2;
+  g.grid = base * g.nsplit;
+  const int rs = R / g.nsplit;
+  g.nw = 1;
+  const int opts[4] = {1, 2, 4, 8};
+  for (int i = 0; i < 4; ++i) {
+    if (rs % (opts[i] * 64) != 0) continue;
+    g.nw = opts[i];
+    if (g.grid * g.nw >= 2048) break;
+  }
+  return g;
+}
+
+int router_splits(int T, int E, int R) { return T > 0 ? router_geom(T, E, R).nsplit : 1; }
+
 hipError_t router_logits(const float* z, const float* wg, float* logits, int T, int E, int R,
                          hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const int mt = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
-  const int rg = (T > 256 && E % 64 == 0) ? 4 : 1;
-  const long grid = (long)((T + 16 * mt - 1) / (16 * mt)) * (E / (16 * rg));
-  int nw = 1;
-  const int opts[4] = {1, 2, 4, 8};
-  for (int i = 0; i < 4; ++i) {
-    if (R % (opts[i] * 64) != 0) continue;
-    nw = opts[i];
-    if (grid * nw >= 2048) break;
-  }
-#define LMOE_RL(NW_, MT_, RG_) \
-  router_logits_kernel<NW_, MT_, RG_><<<grid, NW_ * 64, 0, s>>>(z, wg, logits, T, E, R)
+  const RouterGeom g = router_geom(T, E, R);
+  const long grid = g.grid;
+  const int nsplit = g.nsplit, mt = g.mt, rg = g.rg;
+#define LMOE_RL(NW_, MT_, RG_)                                        \
+  router_logits_kernel<NW_, MT_, RG_><<<grid, NW_ * 64, 0, s>>>(z, wg, logits, T, E, R, nsplit)
 #define LMOE_RL_MT(NW_)                 \
   do {                                  \
     if (rg == 4) LMOE_RL(NW_, 4, 4);    \
@@ -222,7 +272,7 @@ hipError_t router_logits(const float* z, const float* wg, float* logits, int T, 
     else if (mt == 2) LMOE_RL(NW_, 2, 1); \
     else LMOE_RL(NW_, 4, 1);            \
   } while (0)
-  switch (nw) {
+  switch (g.nw) {
     case 1: LMOE_RL_MT(1); break;
     case 2: LMOE_RL_MT(2); break;
     case 4: LMOE_RL_MT(4); break;
@@ -233,12 +283,14 @@ hipError_t router_logits(const float* z, const float* wg, float* logits, int T, 
   return hipGetLastError();
 }
 
-hipError_t router_select(const float* logits, const float* bias, int T, int E, int K, float rho,
-                         int32_t* idx, float* w, hipStream_t s) {
+hipError_t router_select(const float* logits, const float* bias, int T, int E, int R, int K,
+                         float rho, int32_t* idx, float* w, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int grid = (T + 3) / 4;
   const int nj = (E + 63) / 64;
-#define LMOE_RS(NJ_) router_select_kernel<NJ_><<<grid, 256, 0, s>>>(logits, bias, T, E, K, rho, idx, w)
+  const int nsplit = router_splits(T, E, R);
+#define LMOE_RS(NJ_) \
+  router_select_kernel<NJ_><<<grid, 256, 0, s>>>(logits, nsplit, bias, T, E, K, rho, idx, w)
   if (nj <= 1) LMOE_RS(1);
   else if (nj <= 2) LMOE_RS(2);
   else if (nj <= 4) LMOE_RS(4);
