@@ -160,6 +160,9 @@ def main():
     layer.forward_into(inp.x, y, pkg.Taps(expert_counts=counts))
     torch.cuda.synchronize()
     U = int((counts > 0).sum().item())
+    # load balance of the batch: busiest expert over the mean load, idle experts
+    max_vio = float(counts.max().item()) / (T * sh.num_experts_per_tok / sh.n_routed_experts)
+    empty = sh.n_routed_experts - U
     for _ in range(args.warmup):
         layer.forward_into(inp.x, y)
     torch.cuda.synchronize()
@@ -200,6 +203,16 @@ def main():
         layer_ach = layer_bytes / (ms * 1e-3) / 1e9
         layer_roof = {"bound": "hbm", "achieved": round(layer_ach, 1), "unit": "GB/s",
                       "frac": round(layer_ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": layer_bytes}
+        # HBM bytes the counters measured for one whole forward (every stage),
+        # over the forward's wall time; null without a current measurement
+        measured = [measured_traffic(args.workload, st) for st in sb]
+        if measured and all(m is not None for m in measured):
+            mb = sum(measured)
+            layer_roof["measured_bytes"] = mb
+            layer_roof["measured_achieved"] = round(mb / (ms * 1e-3) / 1e9, 1)
+            layer_roof["measured_frac"] = round(mb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        else:
+            layer_roof["measured_bytes"] = None
     else:
         ach = sf[dom] / (stage_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
@@ -231,6 +244,7 @@ def main():
                                f"{sh.moe_shared_expert_intermediate_size}, bf16 weights, "
                                f"fp32 router",
                    "tokens": T, "seed": wl.seed, "unique_experts": U,
+                   "empty_experts": empty, "max_violation": round(max_vio, 3),
                    "parallelism": "single GPU"},
         "roofline": roof,
         "layer_roofline": layer_roof,
