@@ -57,8 +57,11 @@ typedef enum {
 } lmoe_status;
 
 /* Path selection for the expert and projection GEMMs.  AUTO picks by token
- * count (weight streaming for small batches, LDS-tiled MFMA otherwise);
- * the other values force one tiling for every GEMM (used by tests). */
+ * count: weight streaming for small batches, LDS-tiled MFMA otherwise (the
+ * projections split over k into fp32 partial sums while T <= 256, to fill
+ * the GPU); the other values force one tiling for every GEMM (used by tests;
+ * TILED still splits the projections over k when T <= 256).  Results agree
+ * across paths to rounding. */
 typedef enum { LMOE_PATH_AUTO = 0, LMOE_PATH_STREAM = 1, LMOE_PATH_TILED = 2 } lmoe_path;
 
 typedef struct {

@@ -143,4 +143,51 @@ struct ExpDown {
   }
 };
 
+// Split-k view of a dense problem for the LDS-tiled kernel: work-group
+// (x, y) computes tile x of P over the k range [y * klen, (y + 1) * klen) and
+// its epilogue writes fp32 partial sums to part[y][m][n] (mrows rows).  The
+// split index is blockIdx.y, so the tiled kernel runs unchanged on a 2-D
+// grid.  Both k segments of P are handled: K0 of the view is where P's
+// segment boundary falls inside the range (clamped to [0, klen]), and each
+// segment's pointers are advanced to the range start.  klen and P's K0 are
+// multiples of the k tile, so no k tile straddles the boundary.
+template <class P>
+struct SplitK {
+  P p;
+  int klen;
+  float* part;
+  int mrows;
+  static constexpr bool kGatherA = P::kGatherA;
+  __device__ int kstart() const { return blockIdx.y * klen; }
+  __device__ int off1() const {
+    const int v = kstart() - p.K0();
+    return v < 0 ? 0 : v;
+  }
+  __device__ const uint16_t* a_base0() const { return p.a_base0() + kstart(); }
+  __device__ const uint16_t* a_base1() const { return p.a_base1() + off1(); }
+  __device__ long lda0() const { return p.lda0(); }
+  __device__ long lda1() const { return p.lda1(); }
+  __device__ long ldb0() const { return p.ldb0(); }
+  __device__ long ldb1() const { return p.ldb1(); }
+  __host__ __device__ int N() const { return p.N(); }
+  __host__ __device__ int K() const { return klen; }
+  __device__ int K0() const {
+    const int v = p.K0() - kstart();
+    return v < 0 ? 0 : (v > klen ? klen : v);
+  }
+  __device__ const uint16_t* b_row0(int e, int n) const { return p.b_row0(e, n) + kstart(); }
+  __device__ const uint16_t* b_row1(int e, int n) const {
+    const uint16_t* q = p.b_row1(e, n);
+    return q ? q + off1() : nullptr;
+  }
+  __device__ const uint16_t* a_row0(int m) const { return p.a_row0(m) + kstart(); }
+  __device__ const uint16_t* a_row1(int m) const {
+    const uint16_t* q = p.a_row1(m);
+    return q ? q + off1() : nullptr;
+  }
+  __device__ void store(int, int m, int n, f32x4 v) const {
+    *reinterpret_cast<f32x4*>(part + ((size_t)blockIdx.y * mrows + m) * p.N() + n) = v;
+  }
+};
+
 }  // namespace lmoe

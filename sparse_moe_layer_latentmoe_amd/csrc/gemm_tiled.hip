@@ -271,6 +271,55 @@ static hipError_t launch_grouped(const P& p, const Tile* tiles, const int* ntile
 int tiled_block_m() { return kExpBM; }
 int tiled_block_n() { return 256; }
 
+// Sum of the split partial sums in split order (deterministic), then P's own
+// epilogue; one thread per four consecutive columns.
+template <class P>
+__global__ __launch_bounds__(256) void split_reduce_kernel(P p, const float* __restrict__ part,
+                                                           int nsplit, int mrows) {
+  const int N = p.N();
+  const long i = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= (long)mrows * N) return;
+  const int m = i / N, n = i % N;
+  f32x4 v = *reinterpret_cast<const f32x4*>(part + i);
+  for (int q = 1; q < nsplit; ++q)
+    v += *reinterpret_cast<const f32x4*>(part + (size_t)q * mrows * N + i);
+  p.store(0, m, n, v);
+}
+
+template <class P, int BM, int BN, int NS>
+static hipError_t launch_split(const P& p, int T, float* part, int nsplit, hipStream_t s) {
+  const long gx = xcd_grid((long)((T + BM - 1) / BM) * (p.N() / BN));
+  if (gx <= 0) return hipSuccess;
+  const SplitK<P> sp{p, p.K() / nsplit, part, T};
+  tiled_gemm_kernel<SplitK<P>, false, BM, BN, kDenseBK, NS, kWGN>
+      <<<dim3(gx, nsplit), 128 * kWGN, 0, s>>>(sp, T, nullptr, nullptr);
+  const long n4 = (long)T * p.N() / 4;
+  split_reduce_kernel<<<(n4 + 255) / 256, 256, 0, s>>>(p, part, nsplit, T);
+  return hipGetLastError();
+}
+
+// Largest split count <= want (a power of two) whose k range is a whole
+// number of k tiles.
+static int pick_splits(int K, int want) {
+  for (int n = want; n > 1; n /= 2)
+    if (K % (n * kDenseBK) == 0) return n;
+  return 1;
+}
+
+// Tile shapes and split counts measured on the full-shape problems at
+// T = 192 (speculative-verify batch): output projection 256x256 in 8 splits
+// (62 us vs 145 us for the best weight-streaming shape), latent 128x256 with
+// 3 stages in 8 splits (28 vs 39 us), shared up 256x256 in 4 splits
+// (69 vs 96 us).
+hipError_t split_proj_in(const ProjIn& p, float* part, hipStream_t s) {
+  if (p.N() <= 4096)
+    return launch_split<ProjIn, 128, 256, 3>(p, p.T, part, pick_splits(p.K(), kSplitMax), s);
+  return launch_split<ProjIn, 256, 256, 2>(p, p.T, part, pick_splits(p.K(), 4), s);
+}
+hipError_t split_proj_out(const ProjOut& p, float* part, hipStream_t s) {
+  return launch_split<ProjOut, 256, 256, 2>(p, p.T, part, pick_splits(p.K(), kSplitMax), s);
+}
+
 hipError_t tiled_proj_in(const ProjIn& p, hipStream_t s) {
   return launch_dense<ProjIn, kDenseBM, kDenseBN, kDenseBK, kDenseNS>(p, p.T, s);
 }

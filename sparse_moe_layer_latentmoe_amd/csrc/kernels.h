@@ -20,6 +20,8 @@ hipError_t stream_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, i
 hipError_t stream_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles, int max_tiles,
                            hipStream_t s);
 constexpr int kStreamTileM = 16;
+// Dense GEMMs stream weights for batches of at most this many tokens.
+constexpr int kStreamDenseMaxTokens = 64;
 
 // LDS-tiled MFMA GEMMs (many tokens; expert tiles of tiled_block_m() rows;
 // every N must be a multiple of tiled_block_n()).
@@ -31,6 +33,15 @@ hipError_t tiled_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles
                           hipStream_t s);
 int tiled_block_m();
 int tiled_block_n();
+
+// Split-k LDS-tiled dense GEMMs for mid-sized batches (T <= kSplitMaxTokens):
+// up to kSplitMax fp32 partial [T, N] arrays in `part`, then a fixed-order
+// reduction that runs the problem's epilogue.  Same dimension requirements as
+// the tiled GEMMs.
+constexpr int kSplitMax = 8;
+constexpr int kSplitMaxTokens = 256;
+hipError_t split_proj_in(const ProjIn& p, float* part, hipStream_t s);
+hipError_t split_proj_out(const ProjOut& p, float* part, hipStream_t s);
 
 // Router: fp32 logits, then per token sigmoid / bias / top-K / weights.  The
 // logits GEMM may split k over router_splits(T, E, R) partial [T, E] arrays

@@ -81,7 +81,7 @@ long max_tiles(const lmoe_config& c, long T, int tile_m) {
 }
 
 struct Layout {
-  size_t z32, z16, hs, logits, idx, tw, counts, offsets, blockcnt, rows_tok, inv, tiles, ntiles,
+  size_t z32, z16, hs, part, logits, idx, tw, counts, offsets, blockcnt, rows_tok, inv, tiles, ntiles,
       h, o, r16, total;
 };
 
@@ -100,6 +100,13 @@ Layout make_layout(const lmoe_config& c) {
   L.z32 = take(T * R * 4);
   L.z16 = take(T * R * 2);
   L.hs = take(T * S * 2);
+  // split-k partial sums of the dense GEMMs (any batch of at most
+  // kSplitMaxTokens tokens may take the split path when the tiled GEMMs apply)
+  const size_t D = c.hidden_size;
+  L.part = take(tiled_dims_ok(c) ? static_cast<size_t>(kSplitMax) *
+                                       std::min<size_t>(T, kSplitMaxTokens) *
+                                       std::max({R, S, D}) * 4
+                                 : 0);
   L.logits = take(std::max(T, std::min<size_t>(T, router_split_max_tokens()) *
                                   static_cast<size_t>(router_max_splits())) *
                   E * 4);
@@ -286,8 +293,13 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool tiled_ok = tiled_dims_ok(c);
-  const bool dense_tiled =
-      tiled_ok && (c.path == LMOE_PATH_TILED || (c.path == LMOE_PATH_AUTO && T > 256));
+  // Dense GEMMs: weight streaming for few tokens; LDS-tiled above that,
+  // split over k while the batch is too small to fill the GPU with tiles.
+  enum class Dense { kStream, kSplit, kTiled };
+  Dense dense = Dense::kStream;
+  if (tiled_ok && (c.path == LMOE_PATH_TILED ||
+                   (c.path == LMOE_PATH_AUTO && T > kStreamDenseMaxTokens)))
+    dense = T <= kSplitMaxTokens ? Dense::kSplit : Dense::kTiled;
   const bool expert_tiled =
       tiled_ok && (c.path == LMOE_PATH_TILED ||
                    (c.path == LMOE_PATH_AUTO && static_cast<long>(T) * K > 32L * E));
@@ -297,6 +309,21 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   float* z32 = h->at<float>(h->L.z32);
   uint16_t* z16 = h->at<uint16_t>(h->L.z16);
   uint16_t* hs = h->at<uint16_t>(h->L.hs);
+  float* part = h->at<float>(h->L.part);
+  auto proj_in = [&](const ProjIn& p, hipStream_t st) {
+    switch (dense) {
+      case Dense::kStream: return stream_proj_in(p, st);
+      case Dense::kSplit: return split_proj_in(p, part, st);
+      default: return tiled_proj_in(p, st);
+    }
+  };
+  auto proj_out = [&](const ProjOut& p, hipStream_t st) {
+    switch (dense) {
+      case Dense::kStream: return stream_proj_out(p, st);
+      case Dense::kSplit: return split_proj_out(p, part, st);
+      default: return tiled_proj_out(p, st);
+    }
+  };
   float* logits = h->at<float>(h->L.logits);
   int32_t* idx = h->at<int32_t>(h->L.idx);
   float* tw = h->at<float>(h->L.tw);
@@ -329,7 +356,7 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
 
   if (!mark()) return LMOE_ERR_HIP;
   ProjIn platent{x, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, 0, R};
-  if (!ok(dense_tiled ? tiled_proj_in(platent, s) : stream_proj_in(platent, s)))
+  if (!ok(proj_in(platent, s)))
     return LMOE_ERR_HIP;
   // fork after the latent (the router's input) so that it runs alone: the
   // shared expert's up projection then streams on the auxiliary stream while
@@ -338,7 +365,7 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
     return LMOE_ERR_HIP;
   if (ev && !ok(hipEventRecord(ev[kMainStages + 1], h->aux))) return LMOE_ERR_HIP;
   ProjIn pshared{x, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, R, S};
-  if (!ok(dense_tiled ? tiled_proj_in(pshared, h->aux) : stream_proj_in(pshared, h->aux)))
+  if (!ok(proj_in(pshared, h->aux)))
     return LMOE_ERR_HIP;
   if (ev && !ok(hipEventRecord(ev[kMainStages + 2], h->aux))) return LMOE_ERR_HIP;
   if (!ok(hipEventRecord(h->join, h->aux))) return LMOE_ERR_HIP;
@@ -368,7 +395,7 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   // join, then y = r W2^T + Hs Wsd^T
   if (!ok(hipStreamWaitEvent(s, h->join, 0))) return LMOE_ERR_HIP;
   ProjOut pout{r16, hs, h->w.fc2_latent, h->w.shared_down, y, T, D, R, S};
-  if (!ok(dense_tiled ? tiled_proj_out(pout, s) : stream_proj_out(pout, s))) return LMOE_ERR_HIP;
+  if (!ok(proj_out(pout, s))) return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
 
   if (taps) {

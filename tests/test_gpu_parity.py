@@ -58,6 +58,23 @@ def test_medium_both_tilings(dev, path, tokens):
     assert_parity(rep)
 
 
+@pytest.mark.parametrize("tokens", [64, 65, 256, 257])
+def test_dense_gemm_mode_boundaries(dev, tokens):
+    """Automatic path at the token counts where the dense GEMMs switch from
+    weight streaming (T <= 64) to split-k LDS tiles (T <= 256; at this shape
+    the output projection's k range of 1280 splits into 4 ranges of 320, the
+    first of which straddles the boundary between its two k segments at 256)
+    and to whole-k LDS tiles (T > 256)."""
+    wl = medium(tokens)
+    say(f"[medium T={tokens} auto]")
+    inp = li.make_inputs(wl, dev)
+    g = run_gpu(layer_for(wl, inp), inp.x)
+    check_properties(g, wl.shape, tokens)
+    rep = compare(g, li.bf16_bits(inp.x), li.HostWeights(inp, eager_experts=True), wl.shape)
+    say(rep)
+    assert_parity(rep)
+
+
 def test_paths_agree_on_routing(dev):
     wl = medium(300)
     inp = li.make_inputs(wl, dev)
