@@ -63,14 +63,16 @@ def stage_work(sh, T, U):
 
 
 def source_sha256():
-    """Hash of the HIP sources the decode path is built from (every source but
-    the LDS-tiled GEMM, which only runs for large batches), to tell whether
-    stored counter data still describes the kernels being run."""
+    """Hash of the device code the decode path runs (the kernel sources and
+    the device headers; not the LDS-tiled GEMM, which only runs for large
+    batches, nor the host-side launch code), to tell whether stored counter
+    data still describes the kernels being run."""
     import glob
     import hashlib
     h = hashlib.sha256()
+    device = ("gemm_stream.hip", "router.hip", "dispatch.hip", "gemm_problems.h", "lmoe_device.h")
     for f in sorted(glob.glob(os.path.join(ROOT, "sparse_moe_layer_latentmoe_amd", "csrc", "*"))):
-        if os.path.basename(f) == "gemm_tiled.hip":
+        if os.path.basename(f) not in device:
             continue
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:

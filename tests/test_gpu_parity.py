@@ -75,6 +75,23 @@ def test_dense_gemm_mode_boundaries(dev, tokens):
     assert_parity(rep)
 
 
+@pytest.mark.parametrize("tokens,experts,topk", [(100, 1024, 64), (400, 1024, 8)])
+def test_largest_expert_count_and_top_k(dev, tokens, experts, topk):
+    """The largest configuration the ABI accepts: 1024 experts (16 router
+    slots per lane), top-64 (every lane of the selection wave holds a
+    winner); at T = 400 the per-block masks no longer fit one work-group's
+    LDS, so the three-kernel dispatch runs."""
+    sh = li.LayerShape(256, 64, experts, topk, 128, 256, 5.0)
+    wl = li.Workload("max", sh, tokens)
+    say(f"[E={experts} K={topk} T={tokens}]")
+    inp = li.make_inputs(wl, dev)
+    g = run_gpu(layer_for(wl, inp), inp.x)
+    check_properties(g, sh, tokens)
+    rep = compare(g, li.bf16_bits(inp.x), li.HostWeights(inp, eager_experts=True), sh)
+    say(rep)
+    assert_parity(rep)
+
+
 def test_paths_agree_on_routing(dev):
     wl = medium(300)
     inp = li.make_inputs(wl, dev)
