@@ -5,7 +5,9 @@
 // waves (2 along tokens x 4 along weights) each own a (BM/2) x (BN/4)
 // sub-tile of MFMA 16x16x32 tiles.  Two waves per SIMD are needed: measured
 // on MI355X, one wave per SIMD issuing independent 16x16x32 bf16 MFMAs back
-// to back reaches about half of the matrix-core peak, two reach ~90%.
+// to back tops out near 63% of the matrix-core peak however many
+// accumulators it cycles through (16 to 64), two waves reach ~90%.  That
+// caps a wave at 256 registers and its sub-tile at 64 x 128 accumulators.
 //
 // Operands move global -> LDS with gfx950's direct 16-byte loads
 // (global_load_lds_dwordx4), NS stages in flight and no staging registers;
