@@ -33,9 +33,10 @@
  *    the same time.
  *  - the first lmoe_forward on a handle creates one auxiliary HIP stream
  *    (non-blocking, default priority) and two events, used to run the shared
- *    expert's up projection concurrently with the router (forked from
- *    `stream` after the latent projection and joined back before the output
- *    projection); lmoe_destroy releases them.
+ *    expert's up projection concurrently with the latent projection and the
+ *    router (forked from `stream` at the start of the forward for small
+ *    batches, after the latent projection otherwise, and joined back before
+ *    the output projection); lmoe_destroy releases them.
  */
 #ifndef LMOE_H
 #define LMOE_H
@@ -134,7 +135,7 @@ const char *lmoe_status_string(lmoe_status s);
 /* Number of timed stages of lmoe_forward and the name of stage i.  Stages
  * 0..7 run back to back on the forward's stream (the last one, proj_out,
  * includes the wait for the auxiliary stream); stage 8 ("shared_up") is
- * timed on the auxiliary stream and overlaps stages 1..6. */
+ * timed on the auxiliary stream and overlaps the stages before proj_out. */
 int32_t lmoe_num_stages(void);
 const char *lmoe_stage_name(int32_t i);
 

@@ -11,11 +11,12 @@
 //   expert_down    H Wdn[e]^T                                  (Step 6)
 //   combine        r = sum_k w O                               (Step 6 index_add_)
 //   proj_out       y = r W2^T + Hs Wsd^T                       (Step 7)
-// and, forked onto the handle's auxiliary stream after proj_latent and
-// joined before proj_out (the shared expert only needs x):
+// and, forked onto the handle's auxiliary stream (before proj_latent for
+// weight-streaming batches, after it otherwise) and joined before proj_out
+// (the shared expert only needs x):
 //   shared_up      x -> relu(x Wsu^T)^2                        (Step 7)
-// The router/dispatch chain is latency-bound and leaves HBM idle; the
-// shared expert's weight stream fills that time.
+// The latent projection and the router/dispatch chain are latency-bound and
+// leave HBM idle; the shared expert's weight stream fills that time.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -354,21 +355,27 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   };
   auto ok = [](hipError_t e) { return e == hipSuccess; };
 
+  // Shared expert's up projection on the auxiliary stream, forked from `s`
+  // at the current point and joined before proj_out.
+  auto fork_shared = [&]() -> bool {
+    if (!ok(hipEventRecord(h->fork, s)) || !ok(hipStreamWaitEvent(h->aux, h->fork, 0)))
+      return false;
+    if (ev && !ok(hipEventRecord(ev[kMainStages + 1], h->aux))) return false;
+    ProjIn pshared{x, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, R, S};
+    if (!ok(proj_in(pshared, h->aux))) return false;
+    if (ev && !ok(hipEventRecord(ev[kMainStages + 2], h->aux))) return false;
+    return ok(hipEventRecord(h->join, h->aux));
+  };
+  // Weight streaming: fork first, so that the shared weight stream also uses
+  // the bandwidth the short latent projection leaves idle.  Otherwise fork
+  // after the latent projection (the split-k path's partial sums are one
+  // buffer, and the tiled GEMMs would only compete for the same CUs).
+  const bool fork_first = dense == Dense::kStream;
+  if (fork_first && !fork_shared()) return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
   ProjIn platent{x, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, 0, R};
-  if (!ok(proj_in(platent, s)))
-    return LMOE_ERR_HIP;
-  // fork after the latent (the router's input) so that it runs alone: the
-  // shared expert's up projection then streams on the auxiliary stream while
-  // the latency-bound router and dispatch kernels run
-  if (!ok(hipEventRecord(h->fork, s)) || !ok(hipStreamWaitEvent(h->aux, h->fork, 0)))
-    return LMOE_ERR_HIP;
-  if (ev && !ok(hipEventRecord(ev[kMainStages + 1], h->aux))) return LMOE_ERR_HIP;
-  ProjIn pshared{x, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, R, S};
-  if (!ok(proj_in(pshared, h->aux)))
-    return LMOE_ERR_HIP;
-  if (ev && !ok(hipEventRecord(ev[kMainStages + 2], h->aux))) return LMOE_ERR_HIP;
-  if (!ok(hipEventRecord(h->join, h->aux))) return LMOE_ERR_HIP;
+  if (!ok(proj_in(platent, s))) return LMOE_ERR_HIP;
+  if (!fork_first && !fork_shared()) return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
   if (!ok(router_logits(z32, h->w.router, logits, T, E, R, s))) return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
