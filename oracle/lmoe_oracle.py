@@ -12,7 +12,7 @@ Super 技术解读", §2.2) describe it):
     l      = z Wg^T                     (float32)     router gate      (Step 1)
     s      = sigmoid(l)                 (float32)                      (Step 2)
     b      = s + beta                   (float32)     selection only   (Step 2)
-    I_t    = the K largest b_t (single group)                          (Step 3)
+    I_t    = the K largest b_t among the kept groups' experts         (Step 3, §5.5)
     w_t    = rho * s_t[I_t] / (sum s_t[I_t] + 1e-20)                   (Step 4)
     E_e(u) = relu(u Wup[e]^T)^2 Wdn[e]^T  (non-gated MLP)              (Step 6, §5.1)
     r_t    = sum_k w_t,k E_{I_t,k}(z_t)                                (Step 6)
@@ -31,7 +31,11 @@ Readings taken where the pages are silent or disagree:
   with ``sorted=False``, so the order carries no meaning);
 * the 1e-20 is added to the float32 sum before dividing, then the quotient is
   multiplied by rho (Step 4 order);
-* single routing group: the group score step of §5.5 is a no-op.
+* routing groups (§5.5, used when n_group > 1): contiguous groups of
+  E / n_group experts, a group's score is the float32 sum of its two largest
+  biased scores, equal group scores go to the lower group index, and experts
+  of the dropped groups are excluded from the top-K (not given a score of
+  zero); with n_group = 1 the group step is a no-op.
 
 Parity pins (tests/test_oracle_pins.py): a hand-derived micro example
 (tests/golden/worked_example_micro.json), brute-force subset enumeration for
@@ -63,6 +67,8 @@ class OracleConfig:
     moe_intermediate_size: int
     moe_shared_expert_intermediate_size: int
     routed_scaling_factor: float = 5.0
+    n_group: int = 1
+    topk_group: int = 1
 
 
 def bf16_bits_to_f64(bits) -> np.ndarray:
@@ -92,27 +98,63 @@ def router_scores(z32: np.ndarray, Wg: np.ndarray):
     return logits, s
 
 
-def select_experts(s: np.ndarray, beta: np.ndarray, k: int):
-    """Top-K selection on the biased score (Steps 2-3, single group).
+def select_groups(b: np.ndarray, n_group: int, topk_group: int):
+    """Group-limited routing, group step (page "Nemotron 3 Ultra 架构深度拆解
+    报告", CH5 §5.5 items 1-2 and the group-score line of Step 3).
 
-    b = s + beta in float32.  For each token the experts are ranked by b
-    descending, equal b ranked by expert index ascending; the first ``k`` are
-    kept and returned in ascending expert id.  ``gap`` is the difference
-    between the k-th and the (k+1)-th ranked biased scores (+inf if k = E),
-    i.e. how close the token is to a different selection."""
+    The E experts are split into ``n_group`` contiguous groups of E/n_group;
+    a group's score is the sum of its two largest biased scores (float32
+    addition); the ``topk_group`` groups with the largest scores are kept,
+    equal scores ranked by group index ascending.  Returns the mask of
+    experts in kept groups [T, E] and the gap between the last kept and the
+    first dropped group score (+inf if every group is kept)."""
+    t, e = b.shape
+    g = e // n_group
+    bg = np.asarray(b, F32).reshape(t, n_group, g)
+    top2 = -np.sort(-bg, axis=-1)[..., :2]
+    gscore = (top2[..., 0] + top2[..., 1]).astype(F32)
+    gids = np.broadcast_to(np.arange(n_group), gscore.shape)
+    granked = np.lexsort((gids, -gscore), axis=-1)
+    kept = np.zeros((t, n_group), bool)
+    np.put_along_axis(kept, granked[:, :topk_group], True, axis=1)
+    if topk_group < n_group:
+        last = np.take_along_axis(gscore, granked[:, topk_group - 1:topk_group], 1)[:, 0]
+        first_out = np.take_along_axis(gscore, granked[:, topk_group:topk_group + 1], 1)[:, 0]
+        ggap = last.astype(F64) - first_out.astype(F64)
+    else:
+        ggap = np.full(t, np.inf)
+    return np.repeat(kept, g, axis=1), ggap
+
+
+def select_experts(s: np.ndarray, beta: np.ndarray, k: int, n_group: int = 1,
+                   topk_group: int = 1):
+    """Top-K selection on the biased score (Steps 2-3; §5.5 item 3).
+
+    b = s + beta in float32.  For each token the experts of the kept groups
+    (all experts when n_group = 1) are ranked by b descending, equal b ranked
+    by expert index ascending; the first ``k`` are kept and returned in
+    ascending expert id.  Experts of dropped groups cannot be selected.
+    ``gap`` is the smaller of the group gap (``select_groups``) and the
+    difference between the k-th and the (k+1)-th ranked biased scores among
+    the eligible experts (+inf where there is no (k+1)-th), i.e. how close
+    the token is to a different selection."""
     s = np.asarray(s, F32)
     b = (s + np.asarray(beta, F32)[None, :]).astype(F32)
     t, e = b.shape
+    if n_group > 1:
+        eligible, ggap = select_groups(b, n_group, topk_group)
+    else:
+        eligible, ggap = np.ones(b.shape, bool), np.full(t, np.inf)
     expert_ids = np.broadcast_to(np.arange(e), b.shape)
-    ranked = np.lexsort((expert_ids, -b), axis=-1)
+    ranked = np.lexsort((expert_ids, -b, ~eligible), axis=-1)
     idx = np.sort(ranked[:, :k], axis=1)
+    n_eligible = eligible.sum(1)
+    gap = np.full(t, np.inf)
     if k < e:
         bk = np.take_along_axis(b, ranked[:, k - 1:k], 1)[:, 0].astype(F64)
         bk1 = np.take_along_axis(b, ranked[:, k:k + 1], 1)[:, 0].astype(F64)
-        gap = bk - bk1
-    else:
-        gap = np.full(t, np.inf)
-    return idx, b, gap
+        gap = np.where(n_eligible > k, bk - bk1, np.inf)
+    return idx, b, np.minimum(gap, ggap)
 
 
 def renormalize(s: np.ndarray, idx: np.ndarray, rho: float) -> np.ndarray:
@@ -179,7 +221,7 @@ def forward(x_bits, weights, cfg: OracleConfig, forced_idx=None) -> dict:
     z = latent_projection(x, bf16_bits_to_f64(weights.fc1_latent))
     z32 = z.astype(F32)
     logits, s = router_scores(z32, weights.router)
-    idx, b, gap = select_experts(s, weights.router_bias, k)
+    idx, b, gap = select_experts(s, weights.router_bias, k, cfg.n_group, cfg.topk_group)
     if forced_idx is not None:
         idx = np.sort(np.asarray(forced_idx, np.int64), axis=1)
     w = renormalize(s, idx, cfg.routed_scaling_factor)

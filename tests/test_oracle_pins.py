@@ -96,8 +96,8 @@ def _no_scale(s, idx, rho):
 _orig_select = O.select_experts
 
 
-def _select_unbiased(s, beta, k):
-    return _orig_select(s, np.zeros_like(np.asarray(beta)), k)
+def _select_unbiased(s, beta, k, *groups):
+    return _orig_select(s, np.zeros_like(np.asarray(beta)), k, *groups)
 
 
 def _weights_from_biased(s, idx, rho):
@@ -201,6 +201,71 @@ def test_topk_tie_break_lower_index():
     idx, _, _ = O.select_experts(np.zeros((1, 3), np.float32),
                                  np.array([0.0, -0.0, 0.0], np.float32), 1)
     assert idx.tolist() == [[0]]
+
+
+def test_group_routing_worked_example():
+    """§5.5 by hand: 8 experts in 4 groups of 2, keep 2 groups, top-3.
+    Group scores (sum of the two best biased scores): 1.0, 1.0, 0.8, 0.6, so
+    groups 0 and 1 stay and the top-3 of experts {0, 1, 2, 3} is {0, 2, 3}
+    (2 and 3 tie at 0.5; both fit).  Ungrouped, expert 4 (0.8) would win a
+    place; scoring groups by their single best expert would keep groups 0
+    and 2 and select {0, 1, 4} -- so the example tells the three apart."""
+    s = np.array([[0.9, 0.1, 0.5, 0.5, 0.8, 0.0, 0.3, 0.3]], np.float32)
+    beta = np.zeros(8, np.float32)
+    idx, _, gap = O.select_experts(s, beta, 3, n_group=4, topk_group=2)
+    assert idx.tolist() == [[0, 2, 3]]
+    # gap: groups 1.0 vs 0.8 (0.2) is closer than experts 0.5 vs 0.1 (0.4)
+    assert gap[0] == pytest.approx(float(np.float32(0.5) + np.float32(0.5)) - 0.8, abs=1e-7)
+    assert O.select_experts(s, beta, 3)[0].tolist() == [[0, 2, 4]]
+    # equal group scores: the lower group index is kept
+    s2 = np.array([[0.4, 0.4, 0.3, 0.5, 0.7, 0.1]], np.float32)   # groups of 2: 0.8, 0.8, 0.8
+    idx2, _, gap2 = O.select_experts(s2, np.zeros(6, np.float32), 2, n_group=3, topk_group=1)
+    assert idx2.tolist() == [[0, 1]] and gap2[0] == 0.0
+
+
+def test_group_routing_matches_enumeration():
+    """Group score as the best pair sum over the group, kept groups as the
+    group subset with the largest score total, experts as the K-subset of
+    eligible experts with the largest biased-score total: each by exhaustive
+    enumeration, on random scores (no ties)."""
+    rng = np.random.default_rng(7)
+    E, T = 12, 12
+    for n_group in (2, 3, 4, 6):
+        G = E // n_group
+        for topk_group in range(1, n_group + 1):
+            K = min(3, topk_group * G)
+            s = rng.uniform(0, 1, size=(T, E)).astype(np.float32)
+            beta = rng.normal(0, 0.1, size=E).astype(np.float32)
+            idx, b, _ = O.select_experts(s, beta, K, n_group, topk_group)
+            for t in range(T):
+                gs = [max(float(np.float32(b[t, i]) + np.float32(b[t, j]))
+                          for i, j in itertools.combinations(range(g * G, g * G + G), 2))
+                      for g in range(n_group)]
+                kept = max(itertools.combinations(range(n_group), topk_group),
+                           key=lambda c: sum(gs[g] for g in c))
+                elig = [e for e in range(E) if e // G in kept]
+                best = max(itertools.combinations(elig, K),
+                           key=lambda c: sum(float(b[t, e]) for e in c))
+                assert tuple(idx[t]) == best, (n_group, topk_group, t)
+
+
+def test_group_routing_degenerate_cases():
+    rng = np.random.default_rng(3)
+    T, E, K = 20, 16, 4
+    s = rng.uniform(0, 1, size=(T, E)).astype(np.float32)
+    beta = rng.normal(0, 0.1, size=E).astype(np.float32)
+    plain = O.select_experts(s, beta, K)
+    # one group, or every group kept: the plain top-K
+    for n_group, topk_group in [(1, 1), (4, 4), (8, 8)]:
+        g = O.select_experts(s, beta, K, n_group, topk_group)
+        assert np.array_equal(g[0], plain[0]) and np.array_equal(g[2], plain[2])
+    # groups of two with K = 2 * kept groups: exactly the kept groups' experts
+    idx, _, _ = O.select_experts(s, beta, 4, n_group=8, topk_group=2)
+    groups = idx // 2
+    assert np.all(groups[:, 0] == groups[:, 1]) and np.all(groups[:, 2] == groups[:, 3])
+    # in general the selection spans at most topk_group groups
+    idx, _, _ = O.select_experts(s, beta, 5, n_group=4, topk_group=2)
+    assert all(len(set((idx[t] // 4).tolist())) <= 2 for t in range(T))
 
 
 def test_renormalisation_invariants():
