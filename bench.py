@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 METRIC = "LatentMoE layer tokens/s; % HBM roofline (decode) / % bf16 MFMA peak (prefill)"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
-HBM_BOUND = {"tiny", "decode", "mtp_verify"}
+HBM_BOUND = {"tiny", "decode", "mtp_verify", "decode_grouped"}
 
 
 def stage_work(sh, T, U):
@@ -134,7 +134,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode",
-                    choices=["tiny", "decode", "mtp_verify", "prefill", "skewed"])
+                    choices=["tiny", "decode", "mtp_verify", "prefill", "skewed",
+                             "decode_grouped"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

@@ -72,8 +72,10 @@ typedef struct {
   int32_t num_experts_per_tok;                 /* K; 1..min(E, 64) */
   int32_t moe_intermediate_size;               /* F; multiple of 64 */
   int32_t moe_shared_expert_intermediate_size; /* S; multiple of 64 */
-  int32_t n_group;                             /* routing groups: must be 1 */
-  int32_t topk_group;                          /* groups kept: must be 1 */
+  int32_t n_group;    /* routing groups (§5.5): divides E into groups of >= 2
+                         experts (any size when 1); at most 64 */
+  int32_t topk_group; /* groups kept per token: 1..n_group, and
+                         K <= topk_group * E / n_group */
   float routed_scaling_factor;                 /* rho, finite (5.0 in the model) */
   int32_t max_tokens;                          /* largest T a forward may use; sizes the workspace */
   int32_t path;                                /* lmoe_path */

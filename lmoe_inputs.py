@@ -40,6 +40,8 @@ class LayerShape:
     moe_intermediate_size: int
     moe_shared_expert_intermediate_size: int
     routed_scaling_factor: float = 5.0
+    n_group: int = 1
+    topk_group: int = 1
 
 
 @dataclass(frozen=True)
@@ -65,6 +67,8 @@ WORKLOADS = {
     "mtp_verify": Workload("mtp_verify", FULL, 192),
     "prefill": Workload("prefill", FULL, 8192),
     "skewed": Workload("skewed", FULL, 8192, bias_recipe="zipf"),
+    # the same decode batch with group-limited routing: 8 groups of 64 experts, 4 kept
+    "decode_grouped": Workload("decode_grouped", replace(FULL, n_group=8, topk_group=4), 32),
 }
 
 

@@ -122,7 +122,8 @@ def make_config(shape, max_tokens: int, path: int = PATH_AUTO) -> LmoeConfig:
     return LmoeConfig(
         shape.hidden_size, shape.moe_latent_size, shape.n_routed_experts,
         shape.num_experts_per_tok, shape.moe_intermediate_size,
-        shape.moe_shared_expert_intermediate_size, 1, 1,
+        shape.moe_shared_expert_intermediate_size, int(getattr(shape, "n_group", 1)),
+        int(getattr(shape, "topk_group", 1)),
         float(shape.routed_scaling_factor), int(max_tokens), int(path))
 
 

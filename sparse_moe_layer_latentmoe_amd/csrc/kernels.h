@@ -53,8 +53,10 @@ constexpr int router_split_max_tokens() { return 1024; }
 int router_splits(int T, int E, int R);
 hipError_t router_logits(const float* z, const float* wg, float* logits, int T, int E, int R,
                          hipStream_t s);
+// n_group > 1: group-limited selection (at most 64 groups, one per lane).
 hipError_t router_select(const float* logits, const float* bias, int T, int E, int R, int K,
-                         float rho, int32_t* idx, float* w, hipStream_t s);
+                         int n_group, int topk_group, float rho, int32_t* idx, float* w,
+                         hipStream_t s);
 
 // Grouping by expert: counts[E], offsets[E+1], rows_tok[T*K], inv[T*K] and
 // the tile list (tiles of at most tile_m rows) with its length in *ntiles.

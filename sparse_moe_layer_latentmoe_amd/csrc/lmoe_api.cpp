@@ -63,13 +63,22 @@ lmoe_status check_config(const lmoe_config* c) {
       !std::isfinite(c->routed_scaling_factor))
     return LMOE_ERR_INVALID_ARG;
   if (c->path < LMOE_PATH_AUTO || c->path > LMOE_PATH_TILED) return LMOE_ERR_INVALID_ARG;
-  if (c->n_group != 1 || c->topk_group != 1) return LMOE_ERR_UNSUPPORTED;
   if (c->hidden_size % 64 || c->moe_latent_size % 64 || c->moe_intermediate_size % 64 ||
       c->moe_shared_expert_intermediate_size % 64)
     return LMOE_ERR_UNSUPPORTED;
   if (c->n_routed_experts > 1024 || c->n_routed_experts % 16) return LMOE_ERR_UNSUPPORTED;
   if (c->num_experts_per_tok > c->n_routed_experts || c->num_experts_per_tok > 64)
     return LMOE_ERR_UNSUPPORTED;
+  // routing groups (page §5.5): n_group equal contiguous groups of at least
+  // two experts, 1 <= topk_group <= n_group, enough experts in the kept
+  // groups for the top-K; the selection kernel holds one group per lane
+  if (c->n_group < 1 || c->topk_group < 1 || c->topk_group > c->n_group)
+    return LMOE_ERR_INVALID_ARG;
+  if (c->n_routed_experts <= 0 || c->n_routed_experts % c->n_group) return LMOE_ERR_INVALID_ARG;
+  if (c->n_group > 1 && c->n_routed_experts / c->n_group < 2) return LMOE_ERR_INVALID_ARG;
+  if (c->num_experts_per_tok > c->topk_group * (c->n_routed_experts / c->n_group))
+    return LMOE_ERR_INVALID_ARG;
+  if (c->n_group > 64) return LMOE_ERR_UNSUPPORTED;
   if (c->max_tokens > (1 << 22)) return LMOE_ERR_UNSUPPORTED;
   if (c->path == LMOE_PATH_TILED && !tiled_dims_ok(*c)) return LMOE_ERR_UNSUPPORTED;
   return LMOE_OK;
@@ -264,8 +273,8 @@ lmoe_status lmoe_route(lmoe_handle* h, const float* z_f32, int32_t T, int32_t* t
       hipSuccess)
     return LMOE_ERR_HIP;
   if (router_select(logits, h->w.router_bias, T, c.n_routed_experts, c.moe_latent_size,
-                    c.num_experts_per_tok, c.routed_scaling_factor, topk_idx, topk_w,
-                    s) != hipSuccess)
+                    c.num_experts_per_tok, c.n_group, c.topk_group, c.routed_scaling_factor,
+                    topk_idx, topk_w, s) != hipSuccess)
     return LMOE_ERR_HIP;
   return LMOE_OK;
 }
@@ -379,7 +388,8 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   if (!mark()) return LMOE_ERR_HIP;
   if (!ok(router_logits(z32, h->w.router, logits, T, E, R, s))) return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
-  if (!ok(router_select(logits, h->w.router_bias, T, E, R, K, c.routed_scaling_factor, idx, tw, s)))
+  if (!ok(router_select(logits, h->w.router_bias, T, E, R, K, c.n_group, c.topk_group,
+                        c.routed_scaling_factor, idx, tw, s)))
     return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
   if (!ok(dispatch(idx, T, K, E, blockcnt, counts, offsets, rows_tok, inv, tiles, ntiles, tile_m,

@@ -132,23 +132,48 @@ __device__ __forceinline__ uint32_t ordered_bits(float b) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Largest key v such that at least n of the wave's keys (NS slots per lane)
+// are >= v: built bit by bit from the top, each candidate kept if at least n
+// keys reach it, counted with one ballot per slot (no cross-lane data
+// movement).  With keys of 0 for empty slots and n <= the number of nonzero
+// keys, v is the n-th largest key.
+template <int NS>
+__device__ __forceinline__ uint32_t nth_largest_key(const uint32_t (&key)[NS], int n) {
+  uint32_t v = 0u;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = v | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) cnt += __popcll(__ballot(key[j] >= c));
+    if (cnt >= n) v = c;
+  }
+  return v;
+}
+
 // One wavefront per token.  Expert e = 64 j + lane lives in slot j of lane
 // `lane`; its key is the ordered bit pattern of its biased score (0 for slots
-// past E, below every finite score).  The K-th largest key v is built bit by
-// bit from the top: a candidate stays if at least K keys reach it, counted
-// with one ballot per slot (no cross-lane data movement).  The selected set
-// is every key above v plus the lowest-id experts whose key equals v (equal
-// scores go to the lower expert id).  Output order is ascending expert id,
-// the renormalising sum is a plain float32 sum in that order, then
-// w = (s / (sum + 1e-20)) * rho.
+// past E, below every finite score).  The K-th largest key v comes from
+// nth_largest_key; the selected set is every key above v plus the lowest-id
+// experts whose key equals v (equal scores go to the lower expert id).
+// Output order is ascending expert id, the renormalising sum is a plain
+// float32 sum in that order, then w = (s / (sum + 1e-20)) * rho.
+//
+// Routing groups (n_group > 1; page "Nemotron 3 Ultra 架构深度拆解报告",
+// CH5 §5.5): the token's biased scores go to LDS, lane g < n_group takes the
+// two largest of group g (experts [g G, (g + 1) G)) and their float32 sum is
+// the group score; the topk_group best groups are kept the same way as the
+// experts (equal group scores to the lower group index), and the keys of the
+// experts of the other groups are set to 0, so they cannot be selected.
 template <int NJ>
 __global__ __launch_bounds__(256) void router_select_kernel(const float* __restrict__ logits,
                                                            int nsplit,
                                                            const float* __restrict__ bias, int T,
-                                                           int E, int K, float rho,
+                                                           int E, int K, int n_group,
+                                                           int topk_group, float rho,
                                                            int32_t* __restrict__ idx_out,
                                                            float* __restrict__ w_out) {
   __shared__ float ssel[4][64];
+  __shared__ float sb[4][NJ * 64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
   if (t >= T) return;
@@ -174,30 +199,55 @@ __global__ __launch_bounds__(256) void router_select_kernel(const float* __restr
   }
   float s[NJ];
   uint32_t key[NJ];
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = j * 64 + lane;
     if (e < E) {
       s[j] = 1.0f / (1.0f + expf(-l[j]));
-      key[j] = ordered_bits(s[j] + bias[e]);
+      const float b = s[j] + bias[e];
+      key[j] = ordered_bits(b);
+      sb[wv][e] = b;
     } else {
       s[j] = 0.f;
       key[j] = 0u;
     }
   }
-  uint32_t v = 0u;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t c = v | (1u << bit);
-    int cnt = 0;
+  if (n_group > 1) {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int G = E / n_group;
+    uint32_t gkey[1] = {0u};
+    if (lane < n_group) {
+      float t1 = -INFINITY, t2 = -INFINITY;
+      for (int i = 0; i < G; ++i) {
+        const float b = sb[wv][lane * G + i];
+        if (b > t1) {
+          t2 = t1;
+          t1 = b;
+        } else if (b > t2) {
+          t2 = b;
+        }
+      }
+      gkey[0] = ordered_bits(t1 + t2);
+    }
+    const uint32_t gv = nth_largest_key(gkey, topk_group);
+    const int groom = topk_group - __popcll(__ballot(gkey[0] > gv));
+    const uint64_t geq = __ballot(gkey[0] == gv);
+    const bool kept = gkey[0] > gv || (gkey[0] == gv && __popcll(geq & below) < groom);
+    const uint64_t kept_mask = __ballot(kept);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(key[j] >= c));
-    if (cnt >= K) v = c;
+    for (int j = 0; j < NJ; ++j) {
+      const int e = j * 64 + lane;
+      if (e < E && !((kept_mask >> (e / G)) & 1ull)) key[j] = 0u;
+    }
   }
+  const uint32_t v = nth_largest_key(key, K);
   int above = 0;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) above += __popcll(__ballot(key[j] > v));
   int room = K - above;  // experts with key == v still to take, lowest ids first
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int base = 0;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -284,13 +334,15 @@ hipError_t router_logits(const float* z, const float* wg, float* logits, int T, 
 }
 
 hipError_t router_select(const float* logits, const float* bias, int T, int E, int R, int K,
-                         float rho, int32_t* idx, float* w, hipStream_t s) {
+                         int n_group, int topk_group, float rho, int32_t* idx, float* w,
+                         hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const int grid = (T + 3) / 4;
   const int nj = (E + 63) / 64;
   const int nsplit = router_splits(T, E, R);
 #define LMOE_RS(NJ_) \
-  router_select_kernel<NJ_><<<grid, 256, 0, s>>>(logits, nsplit, bias, T, E, K, rho, idx, w)
+  router_select_kernel<NJ_><<<grid, 256, 0, s>>>(logits, nsplit, bias, T, E, K, n_group, \
+                                                  topk_group, rho, idx, w)
   if (nj <= 1) LMOE_RS(1);
   else if (nj <= 2) LMOE_RS(2);
   else if (nj <= 4) LMOE_RS(4);

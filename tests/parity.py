@@ -29,7 +29,8 @@ WEIGHT_FIELDS = ("fc1_latent", "router", "router_bias", "expert_up", "expert_dow
 def oracle_config(sh) -> O.OracleConfig:
     return O.OracleConfig(sh.hidden_size, sh.moe_latent_size, sh.n_routed_experts,
                           sh.num_experts_per_tok, sh.moe_intermediate_size,
-                          sh.moe_shared_expert_intermediate_size, sh.routed_scaling_factor)
+                          sh.moe_shared_expert_intermediate_size, sh.routed_scaling_factor,
+                          sh.n_group, sh.topk_group)
 
 
 def weight_dict(inp) -> dict:
@@ -111,6 +112,10 @@ def check_properties(g: GpuRun, sh, T: int) -> None:
     assert np.all(np.abs(wsum - sh.routed_scaling_factor) <= 1e-5 * sh.routed_scaling_factor)
     assert np.all(g.w > 0)
     assert torch.isfinite(g.y.float()).all()
+    if sh.n_group > 1:
+        # group-limited routing: every token's experts lie in at most topk_group groups
+        G = E // sh.n_group
+        assert max(len(set((row // G).tolist())) for row in g.idx) <= sh.topk_group
 
 
 def assert_parity(rep: Report, max_ties=None) -> None:

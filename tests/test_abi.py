@@ -77,13 +77,21 @@ def test_workspace_size_and_config_checks(lib):
     # at least the expert hidden and output buffers
     assert lib.lmoe_workspace_size(ctypes.byref(full)) > 8192 * 22 * (5120 + 2048) * 2
     assert lib.lmoe_workspace_size(None) == 0
+    # group-limited routing is accepted (4 groups of 4, keep 2, top-4)
+    assert lib.lmoe_workspace_size(ctypes.byref(cfg(n_group=4, topk_group=2))) > 0
     for bad, status in [
         (dict(hidden_size=0), pkg.LMOE_ERR_INVALID_ARG),
         (dict(max_tokens=0), pkg.LMOE_ERR_INVALID_ARG),
         (dict(routed_scaling_factor=float("inf")), pkg.LMOE_ERR_INVALID_ARG),
         (dict(path=7), pkg.LMOE_ERR_INVALID_ARG),
-        (dict(n_group=2), pkg.LMOE_ERR_UNSUPPORTED),
-        (dict(topk_group=2), pkg.LMOE_ERR_UNSUPPORTED),
+        # routing groups: equal groups of >= 2 experts, 1 <= topk_group <= n_group,
+        # K <= experts in the kept groups, at most 64 groups
+        (dict(n_group=0), pkg.LMOE_ERR_INVALID_ARG),
+        (dict(topk_group=2), pkg.LMOE_ERR_INVALID_ARG),            # > n_group = 1
+        (dict(n_group=3), pkg.LMOE_ERR_INVALID_ARG),               # 16 experts
+        (dict(n_group=16, topk_group=4), pkg.LMOE_ERR_INVALID_ARG),  # groups of one
+        (dict(n_group=8, topk_group=1), pkg.LMOE_ERR_INVALID_ARG),   # K = 4 > 2 eligible
+        (dict(n_routed_experts=256, n_group=128, topk_group=2), pkg.LMOE_ERR_UNSUPPORTED),
         (dict(hidden_size=200), pkg.LMOE_ERR_UNSUPPORTED),
         (dict(moe_intermediate_size=96), pkg.LMOE_ERR_UNSUPPORTED),
         (dict(n_routed_experts=2048), pkg.LMOE_ERR_UNSUPPORTED),

@@ -38,7 +38,7 @@ def sample_rows(T, seed):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name", ["decode", "mtp_verify", "prefill", "skewed"])
+@pytest.mark.parametrize("name", ["decode", "mtp_verify", "prefill", "skewed", "decode_grouped"])
 def test_full_shape(full, name):
     dev, w = full
     wl = li.workload(name)

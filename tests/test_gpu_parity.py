@@ -3,6 +3,7 @@ ABI, at sizes the oracle finishes in seconds (several tiles and ragged
 tails), on both GEMM tilings, plus the edge cases of the method."""
 
 import sys
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -88,6 +89,29 @@ def test_largest_expert_count_and_top_k(dev, tokens, experts, topk):
     g = run_gpu(layer_for(wl, inp), inp.x)
     check_properties(g, sh, tokens)
     rep = compare(g, li.bf16_bits(inp.x), li.HostWeights(inp, eager_experts=True), sh)
+    say(rep)
+    assert_parity(rep)
+
+
+@pytest.mark.parametrize("shape,tokens", [
+    # tiny: 8 groups of 2, keep 2, top-4 = exactly the kept groups' experts
+    (replace(li.TINY, n_group=8, topk_group=2), 64),
+    # medium: 4 groups of 8, keep 2, top-6; 8 groups of 4, keep 3, top-6
+    (replace(MEDIUM, n_group=4, topk_group=2), 129),
+    (replace(MEDIUM, n_group=8, topk_group=3), 300),
+    # every group kept: the ungrouped selection
+    (replace(MEDIUM, n_group=4, topk_group=4), 65),
+])
+def test_group_limited_routing(dev, shape, tokens):
+    """Page §5.5: group score = sum of the group's two best biased scores,
+    topk_group groups kept, top-K among their experts."""
+    wl = li.Workload("grouped", shape, tokens)
+    say(f"[groups n={shape.n_group} keep={shape.topk_group} E={shape.n_routed_experts} "
+        f"K={shape.num_experts_per_tok} T={tokens}]")
+    inp = li.make_inputs(wl, dev)
+    g = run_gpu(layer_for(wl, inp), inp.x)
+    check_properties(g, shape, tokens)
+    rep = compare(g, li.bf16_bits(inp.x), li.HostWeights(inp, eager_experts=True), shape)
     say(rep)
     assert_parity(rep)
 
