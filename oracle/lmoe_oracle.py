@@ -42,7 +42,9 @@ Parity pins (tests/test_oracle_pins.py): a hand-derived micro example
 the top-K, closed-form sigmoid values, exact integer GEMMs, the dense
 "every expert on every token" formulation, and the invariants sum(w) = rho,
 K = 1, K = E, x = 0, Wup = 0, identical experts, token-order equivariance and
-the page's parameter/FLOP accounting.  No function here is unpinned.
+the page's parameter/FLOP accounting; the MXFP4 quantiser by hand-worked
+blocks (ties, saturation, zero blocks), exact round trips and its error
+bound.  No function here is unpinned.
 """
 
 from __future__ import annotations
@@ -78,6 +80,60 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     float32 whose high half is ``bits`` and whose low half is zero."""
     u = np.asarray(bits, dtype=np.uint16)
     return (u.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(F64)
+
+
+# Magnitudes of the E2M1 (FP4) element format, by code 0..7 (page "Nemotron 3
+# Ultra 架构深度拆解报告", CH8 §8.1, E2M1 格式: 0, ±0.5, ±1, ±1.5, ±2, ±3, ±4, ±6);
+# code bit 3 is the sign.
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+MX_BLOCK = 32
+
+
+def mxfp4_quantize(w_bits):
+    """Block-scaled FP4 (MXFP4) quantiser of a bf16 matrix [..., K] along its
+    last (input) axis.  The pages fix the element format (E2M1, CH8 §8.1)
+    but give two different block layouts, so the layout is defined here:
+    blocks of 32 consecutive k, each with a power-of-two scale
+    X = 2^e, e = floor(log2 max|w|) - 2 clipped to [-127, 127] (-127 for an
+    all-zero block; 2 is the E2M1 exponent of 6), stored as the byte e + 127;
+    each element is |w| / X rounded to the nearest E2M1 magnitude, ties to
+    the code with a zero mantissa bit (even code), values above 6 clamped to
+    6, with the sign of w unless the magnitude rounds to 0.  Codes pack two
+    per byte, element 2i in the low nibble.  Returns (codes uint8
+    [..., K/2], scales uint8 [..., K/32])."""
+    w = bf16_bits_to_f64(w_bits)
+    K = w.shape[-1]
+    blocks = w.reshape(*w.shape[:-1], K // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blocks).max(-1)
+    _, ex = np.frexp(amax)                        # amax = m 2^ex, 0.5 <= m < 1
+    e = np.where(amax > 0, ex - 1 - 2, -127).clip(-127, 127)
+    a = np.abs(blocks) / np.ldexp(1.0, e)[..., None]
+    dist = np.abs(a[..., None] - E2M1_MAGNITUDES)  # [..., 32, 8]
+    nearest = dist == dist.min(-1, keepdims=True)
+    even = nearest & (np.arange(8) % 2 == 0)
+    mag = np.where(even.any(-1), even.argmax(-1), nearest.argmax(-1))
+    code = mag + 8 * ((blocks < 0) & (mag > 0))
+    flat = code.reshape(*w.shape[:-1], K)
+    codes = (flat[..., 0::2] | (flat[..., 1::2] << 4)).astype(np.uint8)
+    return codes, (e + 127).astype(np.uint8)
+
+
+def mxfp4_dequantize(codes, scales) -> np.ndarray:
+    """Values of MXFP4 codes (``mxfp4_quantize``'s layout), float64 [..., K]."""
+    codes = np.asarray(codes, np.uint8)
+    c = np.stack([codes & 15, codes >> 4], -1).reshape(*codes.shape[:-1], codes.shape[-1] * 2)
+    mag = E2M1_MAGNITUDES[c & 7]
+    val = np.where(c & 8, -mag, mag)
+    K = c.shape[-1]
+    x = np.ldexp(1.0, np.asarray(scales).astype(np.int64) - 127)
+    return (val.reshape(*c.shape[:-1], K // MX_BLOCK, MX_BLOCK) * x[..., None]).reshape(val.shape)
+
+
+def expert_matrix(a) -> np.ndarray:
+    """An expert weight as float64: bf16 bit patterns (uint16) are upcast,
+    float arrays (e.g. dequantised MXFP4 weights) are taken as they are."""
+    a = np.asarray(a)
+    return bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(F64)
 
 
 def latent_projection(x: np.ndarray, W1: np.ndarray) -> np.ndarray:
@@ -184,15 +240,16 @@ def routed_experts(z: np.ndarray, idx: np.ndarray, w: np.ndarray,
     token's row.
 
     ``expert_up[e]`` / ``expert_down[e]`` return bfloat16 bit patterns
-    (uint16) of shape [F, R] / [R, F]; they are upcast one expert at a time.
+    (uint16) of shape [F, R] / [R, F], or float arrays (dequantised low-
+    precision weights); they are upcast one expert at a time.
     Experts are visited in ascending id, so each token accumulates its
     contributions in ascending expert order."""
     z = np.asarray(z, F64)
     r = np.zeros_like(z)
     for e in np.unique(idx):
         tok, pos = np.nonzero(idx == e)
-        o = expert_mlp(z[tok], bf16_bits_to_f64(expert_up[int(e)]),
-                       bf16_bits_to_f64(expert_down[int(e)]))
+        o = expert_mlp(z[tok], expert_matrix(expert_up[int(e)]),
+                       expert_matrix(expert_down[int(e)]))
         r[tok] += np.asarray(w, F64)[tok, pos][:, None] * o
     return r
 

@@ -268,6 +268,108 @@ def test_group_routing_degenerate_cases():
     assert all(len(set((idx[t] // 4).tolist())) <= 2 for t in range(T))
 
 
+def _bf16(vals):
+    """bf16 bit patterns of values that bf16 represents exactly."""
+    v = np.asarray(vals, np.float32)
+    b = (v.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(O.bf16_bits_to_f64(b), v.astype(np.float64))
+    return b
+
+
+def test_e2m1_magnitudes_are_the_pages_list():
+    # Ultra teardown CH8 §8.1: 0, ±0.5, ±1, ±1.5, ±2, ±3, ±4, ±6
+    assert O.E2M1_MAGNITUDES.tolist() == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+
+
+def test_mxfp4_worked_block():
+    """By hand: max |w| = 3 gives e = floor(log2 3) - 2 = -1, X = 0.5, scale
+    byte 126; |w| / X = 6, 5, 3.5, 2.5, 1.75, 1.25, 0.75, 0.25, 0.5, 0.125:
+    5, 3.5, 2.5, 1.75, 1.25, 0.75 and 0.25 are ties and go to the even code
+    (4, 4, 2, 2, 1, 1, 0), -0.0625 rounds to an unsigned zero."""
+    w = np.zeros(32, np.float32)
+    w[:10] = [3.0, 2.5, 1.75, 1.25, 0.875, 0.625, 0.375, 0.125, -0.25, -0.0625]
+    codes, scales = O.mxfp4_quantize(_bf16(w)[None])
+    assert scales.tolist() == [[126]]
+    assert codes[0, :5].tolist() == [7 | 6 << 4, 6 | 4 << 4, 4 | 2 << 4, 2 | 0 << 4, 9 | 0 << 4]
+    assert not codes[0, 5:].any()
+    assert O.mxfp4_dequantize(codes, scales)[0, :10].tolist() == [
+        3.0, 2.0, 2.0, 1.0, 1.0, 0.5, 0.5, 0.0, -0.25, 0.0]
+
+
+def test_mxfp4_saturation_zero_block_and_round_trip():
+    # max |w| = 1.9375 < 2: e = -2, X = 0.25, 1.9375 / X = 7.75 clamps to 6 -> 1.5
+    w = np.full(32, 0.5, np.float32)
+    w[3] = -1.9375
+    codes, scales = O.mxfp4_quantize(_bf16(w)[None])
+    assert scales.tolist() == [[125]]
+    back = O.mxfp4_dequantize(codes, scales)[0]
+    assert back[3] == -1.5 and np.all(np.delete(back, 3) == 0.5)
+    # all-zero block: smallest scale, zero codes
+    codes, scales = O.mxfp4_quantize(np.zeros((2, 64), np.uint16))
+    assert scales.tolist() == [[0, 0], [0, 0]] and not codes.any()
+    assert not O.mxfp4_dequantize(codes, scales).any()
+    # values already on the grid at the block's own scale come back exactly
+    rng = np.random.default_rng(5)
+    for e in (-9, -1, 0, 4):
+        mags = O.E2M1_MAGNITUDES[rng.integers(0, 8, size=(3, 64))]
+        mags[:, ::32] = 6.0                       # pin the block maximum
+        v = (mags * rng.choice([-1, 1], size=mags.shape) * 2.0 ** e).astype(np.float32)
+        c, sc = O.mxfp4_quantize(_bf16(v))
+        assert np.all(sc == e + 127)
+        assert np.array_equal(O.mxfp4_dequantize(c, sc), v.astype(np.float64))
+
+
+def test_mxfp4_error_bound_and_monotone():
+    """Random bf16 weights: within a block the error is at most X (half the
+    widest grid spacing, 4 -> 6) below 6X and at most 2X above it, and the
+    quantiser is monotone in w."""
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    b = (w.view(np.uint32) >> 16).astype(np.uint16)
+    wv = O.bf16_bits_to_f64(b)
+    codes, scales = O.mxfp4_quantize(b)
+    back = O.mxfp4_dequantize(codes, scales)
+    X = np.repeat(np.ldexp(1.0, scales.astype(int) - 127), 32, axis=1)
+    a = np.abs(wv) / X
+    err = np.abs(back - wv) / X
+    assert np.all(err[a <= 6] <= 1.0) and np.all(err[a > 6] <= 2.0)
+    assert np.all(a < 8)
+    for r in range(4):
+        for blk in range(8):
+            sl = slice(32 * blk, 32 * blk + 32)
+            order = np.argsort(wv[r, sl], kind="stable")
+            assert np.all(np.diff(back[r, sl][order]) >= 0)
+
+
+def test_mxfp4_planted_tie_rule_fails_worked_block(monkeypatch):
+    """Ties to the lower magnitude instead of the even code: caught."""
+    def lower_ties(w_bits):
+        w = O.bf16_bits_to_f64(w_bits)
+        K = w.shape[-1]
+        blocks = w.reshape(*w.shape[:-1], K // 32, 32)
+        amax = np.abs(blocks).max(-1)
+        _, ex = np.frexp(amax)
+        e = np.where(amax > 0, ex - 3, -127).clip(-127, 127)
+        a = np.abs(blocks) / np.ldexp(1.0, e)[..., None]
+        mag = np.abs(a[..., None] - O.E2M1_MAGNITUDES).argmin(-1)
+        code = (mag + 8 * ((blocks < 0) & (mag > 0))).reshape(*w.shape[:-1], K)
+        return (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8), (e + 127).astype(np.uint8)
+    monkeypatch.setattr(O, "mxfp4_quantize", lower_ties)
+    with pytest.raises(AssertionError):
+        test_mxfp4_worked_block()
+
+
+def test_float_expert_weights_equal_their_bf16_bits():
+    """The forward takes expert weights as bf16 bits or as float arrays (the
+    dequantised low-precision weights); the same values give the same
+    layer output either way (worked example)."""
+    g, cfg, x, w = micro_case()
+    w2 = SimpleNamespace(**vars(w))
+    w2.expert_up = [O.bf16_bits_to_f64(m) for m in w.expert_up]
+    w2.expert_down = [O.bf16_bits_to_f64(m) for m in w.expert_down]
+    check_micro(O.forward(x, w2, cfg), g["expected"])
+
+
 def test_renormalisation_invariants():
     rng = np.random.default_rng(2)
     E, T = 64, 200
