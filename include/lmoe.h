@@ -65,6 +65,14 @@ typedef enum {
  * across paths to rounding. */
 typedef enum { LMOE_PATH_AUTO = 0, LMOE_PATH_STREAM = 1, LMOE_PATH_TILED = 2 } lmoe_path;
 
+/* Storage of the routed experts' weights.  BF16: expert_up / expert_down.
+ * MXFP4 (block-scaled FP4 with the E2M1 elements of CH8 §8.1 of the page
+ * "Nemotron 3 Ultra 架构深度拆解报告"; block layout: lmoe_quantize_mxfp4):
+ * the *_mxfp4 / *_scale fields; the expert GEMMs decode the weights exactly
+ * to bf16 and always stream them (the decode-oriented format; R and F must
+ * be multiples of 128).  Everything else stays bf16 / fp32. */
+typedef enum { LMOE_EXPERTS_BF16 = 0, LMOE_EXPERTS_MXFP4 = 1 } lmoe_expert_format;
+
 typedef struct {
   int32_t hidden_size;                         /* D; multiple of 64 */
   int32_t moe_latent_size;                     /* R; multiple of 64 */
@@ -79,6 +87,7 @@ typedef struct {
   float routed_scaling_factor;                 /* rho, finite (5.0 in the model) */
   int32_t max_tokens;                          /* largest T a forward may use; sizes the workspace */
   int32_t path;                                /* lmoe_path */
+  int32_t expert_format;                       /* lmoe_expert_format */
 } lmoe_config;
 
 /* Device pointers; the handle borrows them and they must outlive it. */
@@ -91,6 +100,11 @@ typedef struct {
   const uint16_t *fc2_latent;  /* bf16 [D, R] */
   const uint16_t *shared_up;   /* bf16 [S, D] */
   const uint16_t *shared_down; /* bf16 [D, S] */
+  /* MXFP4 experts (expert_format = LMOE_EXPERTS_MXFP4; else unused): */
+  const uint8_t *expert_up_mxfp4;   /* [E, F, R/2] codes, 16-byte aligned */
+  const uint8_t *expert_up_scale;   /* [E, F, R/32] block scales */
+  const uint8_t *expert_down_mxfp4; /* [E, R, F/2] codes, 16-byte aligned */
+  const uint8_t *expert_down_scale; /* [E, R, F/32] block scales */
 } lmoe_weights;
 
 /* Optional device outputs of intermediate values (tests, monitoring).  Any
@@ -124,6 +138,19 @@ lmoe_status lmoe_forward(lmoe_handle *h, const uint16_t *x, int32_t T, uint16_t 
  * write topk_idx [T, K] (ascending expert id) and topk_w [T, K]. */
 lmoe_status lmoe_route(lmoe_handle *h, const float *z_f32, int32_t T, int32_t *topk_idx,
                        float *topk_w, void *stream);
+
+/* MXFP4 quantiser for expert weights: w is bf16 [rows, cols] (row-major,
+ * cols a multiple of 32, 16-byte aligned); writes codes [rows, cols/2]
+ * (16-byte aligned; element 2i of a row in the low nibble of byte i, code
+ * = sign bit 3 | E2M1 magnitude code 0..7 for 0, 0.5, 1, 1.5, 2, 3, 4, 6)
+ * and scales [rows, cols/32] (block b of a row holds elements 32b..32b+31
+ * and its value is 2^(scale - 127)).  Per block: e = floor(log2 max|w|) - 2
+ * clipped to [-127, 127] (-127 for an all-zero block); each element is
+ * |w| / 2^e rounded to the nearest E2M1 magnitude, ties to the even code,
+ * clamped at 6, signed unless it rounds to 0.  Inputs must be finite.
+ * Device pointers; asynchronous on `stream`. */
+lmoe_status lmoe_quantize_mxfp4(const uint16_t *w, int64_t rows, int32_t cols, uint8_t *codes,
+                                uint8_t *scales, void *stream);
 
 /* Free the handle and the auxiliary stream and events it created (no
  * device memory is freed: the caller owns all of it).  NULL is a no-op. */

@@ -27,11 +27,12 @@ LMOE_ERR_WORKSPACE = -4
 LMOE_ERR_HIP = -5
 
 PATH_AUTO, PATH_STREAM, PATH_TILED = 0, 1, 2
+EXPERTS_BF16, EXPERTS_MXFP4 = 0, 1
 
 EXPORTED = (
     "lmoe_workspace_size", "lmoe_create", "lmoe_forward", "lmoe_route", "lmoe_destroy",
     "lmoe_status_string", "lmoe_num_stages", "lmoe_stage_name", "lmoe_profile_begin",
-    "lmoe_profile_end",
+    "lmoe_profile_end", "lmoe_quantize_mxfp4",
 )
 
 
@@ -48,13 +49,15 @@ class LmoeConfig(ctypes.Structure):
         ("routed_scaling_factor", ctypes.c_float),
         ("max_tokens", ctypes.c_int32),
         ("path", ctypes.c_int32),
+        ("expert_format", ctypes.c_int32),
     ]
 
 
 class LmoeWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "fc1_latent", "router", "router_bias", "expert_up", "expert_down",
-        "fc2_latent", "shared_up", "shared_down")]
+        "fc2_latent", "shared_up", "shared_down", "expert_up_mxfp4", "expert_up_scale",
+        "expert_down_mxfp4", "expert_down_scale")]
 
 
 class LmoeTaps(ctypes.Structure):
@@ -104,6 +107,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lmoe_profile_end.argtypes = [P, ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
                                      ctypes.POINTER(ctypes.c_int32)]
     lib.lmoe_profile_end.restype = ctypes.c_int
+    lib.lmoe_quantize_mxfp4.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P, P]
+    lib.lmoe_quantize_mxfp4.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -117,14 +122,15 @@ def stage_names() -> list:
     return [lib.lmoe_stage_name(i).decode() for i in range(lib.lmoe_num_stages())]
 
 
-def make_config(shape, max_tokens: int, path: int = PATH_AUTO) -> LmoeConfig:
+def make_config(shape, max_tokens: int, path: int = PATH_AUTO,
+                expert_format: int = EXPERTS_BF16) -> LmoeConfig:
     """Config struct from any object with the model's config-key attributes."""
     return LmoeConfig(
         shape.hidden_size, shape.moe_latent_size, shape.n_routed_experts,
         shape.num_experts_per_tok, shape.moe_intermediate_size,
         shape.moe_shared_expert_intermediate_size, int(getattr(shape, "n_group", 1)),
         int(getattr(shape, "topk_group", 1)),
-        float(shape.routed_scaling_factor), int(max_tokens), int(path))
+        float(shape.routed_scaling_factor), int(max_tokens), int(path), int(expert_format))
 
 
 def workspace_size(cfg: LmoeConfig) -> int:
@@ -156,6 +162,23 @@ class Taps:
                         _ptr(self.expert_counts), _ptr(self.r_latent))
 
 
+def quantize_mxfp4(w, stream=None):
+    """MXFP4 codes and block scales of a bf16 matrix [..., K] (K a multiple
+    of 32), quantised along its last axis by the library's kernel:
+    (codes uint8 [..., K/2], scales uint8 [..., K/32]) on w's device."""
+    import torch
+    w = w.contiguous()
+    K = int(w.shape[-1])
+    rows = w.numel() // K if K else 0
+    codes = torch.empty(*w.shape[:-1], K // 2, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(*w.shape[:-1], K // 32, dtype=torch.uint8, device=w.device)
+    st = load_library().lmoe_quantize_mxfp4(_ptr(w), rows, K, _ptr(codes), _ptr(scales),
+                                            _stream_handle(stream))
+    if st != LMOE_OK:
+        raise LmoeError(st, "lmoe_quantize_mxfp4")
+    return codes, scales
+
+
 class LatentMoE:
     """One LatentMoE layer bound to caller-owned device weights.
 
@@ -165,18 +188,18 @@ class LatentMoE:
     allocates."""
 
     def __init__(self, shape, weights: dict, max_tokens: int, path: int = PATH_AUTO,
-                 device=None):
+                 device=None, expert_format: int = EXPERTS_BF16):
         import torch
         self.lib = load_library()
         self.shape = shape
-        self.cfg = make_config(shape, max_tokens, path)
+        self.cfg = make_config(shape, max_tokens, path, expert_format)
         ws_bytes = workspace_size(self.cfg)
         if ws_bytes == 0:
             raise LmoeError(LMOE_ERR_UNSUPPORTED, "lmoe_workspace_size")
         dev = device if device is not None else weights["fc1_latent"].device
         self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-        self.weights = {k: v.contiguous() for k, v in weights.items()}
-        self.wstruct = LmoeWeights(*[_ptr(self.weights[n]) for n, _ in LmoeWeights._fields_])
+        self.weights = {k: v.contiguous() for k, v in weights.items() if v is not None}
+        self.wstruct = LmoeWeights(*[_ptr(self.weights.get(n)) for n, _ in LmoeWeights._fields_])
         h = ctypes.c_void_p()
         st = self.lib.lmoe_create(ctypes.byref(self.cfg), ctypes.byref(self.wstruct),
                                   _ptr(self.workspace), ws_bytes, ctypes.byref(h))

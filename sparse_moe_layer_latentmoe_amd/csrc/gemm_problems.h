@@ -143,6 +143,51 @@ struct ExpDown {
   }
 };
 
+// Expert GEMMs with MXFP4 weights (block-scaled FP4; the layout of
+// lmoe_quantize_mxfp4): weight row n of expert e is K/2 code bytes (element
+// 2i in the low nibble of byte i) and K/32 scale bytes (2^(byte - 127) per
+// block of 32 consecutive k).  Activations stay bf16.
+struct ExpUpMx {
+  const uint16_t* z16;
+  const int32_t* rows_tok;
+  const uint8_t* codes;   // [E, F, R/2]
+  const uint8_t* scales;  // [E, F, R/32]
+  uint16_t* h;            // [slots, F]
+  int R, F;
+  __host__ __device__ int N() const { return F; }
+  __host__ __device__ int K() const { return R; }
+  __device__ const uint8_t* codes_row(int e, int n) const {
+    return codes + ((size_t)e * F + n) * (R / 2);
+  }
+  __device__ const uint8_t* scales_row(int e, int n) const {
+    return scales + ((size_t)e * F + n) * (R / 32);
+  }
+  __device__ const uint16_t* a_row(int p) const { return z16 + (size_t)rows_tok[p] * R; }
+  __device__ void store(int, int p, int n, f32x4 v) const {
+    store4_bf16_relu_sq(h + (size_t)p * F + n, v);
+  }
+};
+
+struct ExpDownMx {
+  const uint16_t* h;      // [slots, F]
+  const uint8_t* codes;   // [E, R, F/2]
+  const uint8_t* scales;  // [E, R, F/32]
+  uint16_t* o;            // [slots, R]
+  int R, F;
+  __host__ __device__ int N() const { return R; }
+  __host__ __device__ int K() const { return F; }
+  __device__ const uint8_t* codes_row(int e, int n) const {
+    return codes + ((size_t)e * R + n) * (F / 2);
+  }
+  __device__ const uint8_t* scales_row(int e, int n) const {
+    return scales + ((size_t)e * R + n) * (F / 32);
+  }
+  __device__ const uint16_t* a_row(int p) const { return h + (size_t)p * F; }
+  __device__ void store(int, int p, int n, f32x4 v) const {
+    store4_bf16(o + (size_t)p * R + n, v);
+  }
+};
+
 // Split-k view of a dense problem for the LDS-tiled kernel: work-group
 // (x, y) computes tile x of P over the k range [y * klen, (y + 1) * klen) and
 // its epilogue writes fp32 partial sums to part[y][m][n] (mrows rows).  The

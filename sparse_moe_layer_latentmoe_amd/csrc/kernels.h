@@ -10,6 +10,8 @@ struct ProjIn;
 struct ProjOut;
 struct ExpUp;
 struct ExpDown;
+struct ExpUpMx;
+struct ExpDownMx;
 struct Tile;
 
 // Weight-streaming GEMMs (few tokens; expert tiles of 16 rows).
@@ -42,6 +44,16 @@ constexpr int kSplitMax = 8;
 constexpr int kSplitMaxTokens = 256;
 hipError_t split_proj_in(const ProjIn& p, float* part, hipStream_t s);
 hipError_t split_proj_out(const ProjOut& p, float* part, hipStream_t s);
+
+// MXFP4 expert weights: quantiser (rows x cols bf16 -> codes rows x cols/2,
+// scales rows x cols/32; cols a multiple of 32) and the weight-streaming
+// expert GEMMs (K a multiple of 128, N a multiple of 64).
+hipError_t mxfp4_quantize(const uint16_t* w, long rows, int cols, uint8_t* codes,
+                          uint8_t* scales, hipStream_t s);
+hipError_t stream_mx_exp_up(const ExpUpMx& p, const Tile* tiles, const int* ntiles,
+                            int max_tiles, hipStream_t s);
+hipError_t stream_mx_exp_down(const ExpDownMx& p, const Tile* tiles, const int* ntiles,
+                              int max_tiles, hipStream_t s);
 
 // Router: fp32 logits, then per token sigmoid / bias / top-K / weights.  The
 // logits GEMM may split k over router_splits(T, E, R) partial [T, E] arrays

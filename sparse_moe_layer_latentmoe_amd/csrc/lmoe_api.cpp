@@ -63,6 +63,8 @@ lmoe_status check_config(const lmoe_config* c) {
       !std::isfinite(c->routed_scaling_factor))
     return LMOE_ERR_INVALID_ARG;
   if (c->path < LMOE_PATH_AUTO || c->path > LMOE_PATH_TILED) return LMOE_ERR_INVALID_ARG;
+  if (c->expert_format != LMOE_EXPERTS_BF16 && c->expert_format != LMOE_EXPERTS_MXFP4)
+    return LMOE_ERR_INVALID_ARG;
   if (c->hidden_size % 64 || c->moe_latent_size % 64 || c->moe_intermediate_size % 64 ||
       c->moe_shared_expert_intermediate_size % 64)
     return LMOE_ERR_UNSUPPORTED;
@@ -79,6 +81,10 @@ lmoe_status check_config(const lmoe_config* c) {
   if (c->num_experts_per_tok > c->topk_group * (c->n_routed_experts / c->n_group))
     return LMOE_ERR_INVALID_ARG;
   if (c->n_group > 64) return LMOE_ERR_UNSUPPORTED;
+  // MXFP4 experts: the streaming kernel covers 128 k per step (4 blocks)
+  if (c->expert_format == LMOE_EXPERTS_MXFP4 &&
+      (c->moe_latent_size % 128 || c->moe_intermediate_size % 128))
+    return LMOE_ERR_UNSUPPORTED;
   if (c->max_tokens > (1 << 22)) return LMOE_ERR_UNSUPPORTED;
   if (c->path == LMOE_PATH_TILED && !tiled_dims_ok(*c)) return LMOE_ERR_UNSUPPORTED;
   return LMOE_OK;
@@ -167,13 +173,22 @@ lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, void* wor
   *out = nullptr;
   const lmoe_status st = check_config(cfg);
   if (st != LMOE_OK) return st;
-  if (!w || !w->fc1_latent || !w->router || !w->router_bias || !w->expert_up ||
-      !w->expert_down || !w->fc2_latent || !w->shared_up || !w->shared_down)
+  if (!w || !w->fc1_latent || !w->router || !w->router_bias || !w->fc2_latent ||
+      !w->shared_up || !w->shared_down)
     return LMOE_ERR_INVALID_ARG;
-  const void* ptrs[8] = {w->fc1_latent, w->router,     w->router_bias, w->expert_up,
-                         w->expert_down, w->fc2_latent, w->shared_up,  w->shared_down};
+  const void* ptrs[6] = {w->fc1_latent, w->router,    w->router_bias,
+                         w->fc2_latent, w->shared_up, w->shared_down};
   for (const void* p : ptrs)
     if (!aligned16(p)) return LMOE_ERR_INVALID_ARG;
+  if (cfg->expert_format == LMOE_EXPERTS_MXFP4) {
+    if (!w->expert_up_mxfp4 || !w->expert_up_scale || !w->expert_down_mxfp4 ||
+        !w->expert_down_scale || !aligned16(w->expert_up_mxfp4) ||
+        !aligned16(w->expert_down_mxfp4))
+      return LMOE_ERR_INVALID_ARG;
+  } else if (!w->expert_up || !w->expert_down || !aligned16(w->expert_up) ||
+             !aligned16(w->expert_down)) {
+    return LMOE_ERR_INVALID_ARG;
+  }
   const Layout L = make_layout(*cfg);
   if (!workspace || workspace_bytes < L.total) return LMOE_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return LMOE_ERR_WORKSPACE;
@@ -257,6 +272,18 @@ lmoe_status lmoe_profile_end(lmoe_handle* h, float* ms, int32_t n_stages, int32_
   return st;
 }
 
+lmoe_status lmoe_quantize_mxfp4(const uint16_t* w, int64_t rows, int32_t cols, uint8_t* codes,
+                                uint8_t* scales, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32) return LMOE_ERR_INVALID_ARG;
+  if (rows == 0) return LMOE_OK;
+  if (!w || !codes || !scales || !aligned16(w) || !aligned16(codes)) return LMOE_ERR_INVALID_ARG;
+  if (rows > (int64_t{1} << 40) / cols) return LMOE_ERR_INVALID_ARG;
+  return mxfp4_quantize(w, static_cast<long>(rows), cols, codes, scales,
+                        static_cast<hipStream_t>(stream)) == hipSuccess
+             ? LMOE_OK
+             : LMOE_ERR_HIP;
+}
+
 lmoe_status lmoe_route(lmoe_handle* h, const float* z_f32, int32_t T, int32_t* topk_idx,
                        float* topk_w, void* stream) {
   if (!h) return LMOE_ERR_INVALID_ARG;
@@ -310,9 +337,11 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   if (tiled_ok && (c.path == LMOE_PATH_TILED ||
                    (c.path == LMOE_PATH_AUTO && T > kStreamDenseMaxTokens)))
     dense = T <= kSplitMaxTokens ? Dense::kSplit : Dense::kTiled;
+  const bool mxfp4 = c.expert_format == LMOE_EXPERTS_MXFP4;
   const bool expert_tiled =
-      tiled_ok && (c.path == LMOE_PATH_TILED ||
-                   (c.path == LMOE_PATH_AUTO && static_cast<long>(T) * K > 32L * E));
+      !mxfp4 && tiled_ok &&
+      (c.path == LMOE_PATH_TILED ||
+       (c.path == LMOE_PATH_AUTO && static_cast<long>(T) * K > 32L * E));
   const int tile_m = expert_tiled ? tiled_block_m() : kStreamTileM;
   const int ntile_max = static_cast<int>(max_tiles(c, T, tile_m));
 
@@ -396,15 +425,25 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
                    s)))
     return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
-  ExpUp pup{z16, rows_tok, h->w.expert_up, H, R, F};
-  if (!ok(expert_tiled ? tiled_exp_up(pup, tiles, ntiles, ntile_max, s)
-                       : stream_exp_up(pup, tiles, ntiles, ntile_max, s)))
-    return LMOE_ERR_HIP;
+  if (mxfp4) {
+    ExpUpMx pup{z16, rows_tok, h->w.expert_up_mxfp4, h->w.expert_up_scale, H, R, F};
+    if (!ok(stream_mx_exp_up(pup, tiles, ntiles, ntile_max, s))) return LMOE_ERR_HIP;
+  } else {
+    ExpUp pup{z16, rows_tok, h->w.expert_up, H, R, F};
+    if (!ok(expert_tiled ? tiled_exp_up(pup, tiles, ntiles, ntile_max, s)
+                         : stream_exp_up(pup, tiles, ntiles, ntile_max, s)))
+      return LMOE_ERR_HIP;
+  }
   if (!mark()) return LMOE_ERR_HIP;
-  ExpDown pdn{H, h->w.expert_down, O, R, F};
-  if (!ok(expert_tiled ? tiled_exp_down(pdn, tiles, ntiles, ntile_max, s)
-                       : stream_exp_down(pdn, tiles, ntiles, ntile_max, s)))
-    return LMOE_ERR_HIP;
+  if (mxfp4) {
+    ExpDownMx pdn{H, h->w.expert_down_mxfp4, h->w.expert_down_scale, O, R, F};
+    if (!ok(stream_mx_exp_down(pdn, tiles, ntiles, ntile_max, s))) return LMOE_ERR_HIP;
+  } else {
+    ExpDown pdn{H, h->w.expert_down, O, R, F};
+    if (!ok(expert_tiled ? tiled_exp_down(pdn, tiles, ntiles, ntile_max, s)
+                         : stream_exp_down(pdn, tiles, ntiles, ntile_max, s)))
+      return LMOE_ERR_HIP;
+  }
   if (!mark()) return LMOE_ERR_HIP;
   if (!ok(combine(O, inv, tw, T, K, R, r16, taps ? taps->r_latent : nullptr, s)))
     return LMOE_ERR_HIP;

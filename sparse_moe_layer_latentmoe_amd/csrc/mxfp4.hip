@@ -1,0 +1,224 @@
+// Block-scaled FP4 (MXFP4) expert weights for the weight-streaming path.
+//
+// The pages train the experts in FP4 with E2M1 elements (page "Nemotron 3
+// Ultra 架构深度拆解报告", CH8 §8.1: values 0, ±0.5, ±1, ±1.5, ±2, ±3, ±4,
+// ±6) but give two different block layouts, so the layout is fixed here, as
+// the one gfx950 decodes in hardware: blocks of 32 consecutive k of a weight
+// row, each with a power-of-two scale 2^(byte - 127).  Decoding is exact
+// into bf16, so the expert GEMMs run the bf16 MFMA on the exact dequantised
+// weights (weights 4.25 bits, activations bf16).
+//
+//   quantise  one thread per block: X = 2^e with e = floor(log2 max|w|) - 2
+//             (clipped to [-127, 127]; -127 for an all-zero block), each
+//             element |w| / X rounded to the nearest E2M1 magnitude with
+//             ties to the even code (zero mantissa bit), clamped at 6,
+//             signed unless it rounds to 0.
+//   stream    like the bf16 weight-streaming GEMM, with one lane loading the
+//             16 code bytes of one block (32 k of one row) plus its scale
+//             byte: the four lanes of a row cover 128 consecutive k, and MFMA
+//             step u takes code bytes 4u..4u+3 of every lane, converted with
+//             v_cvt_scalef32_pk_bf16_fp4 (element 0 = low nibble, measured).
+//             The token fragments are loaded at the same k, so both MFMA
+//             operands agree on which 32 k a step sums over.
+#include <algorithm>
+
+#include "gemm_problems.h"
+#include "kernels.h"
+
+namespace lmoe {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// E2M1 magnitude code of a = |w| / X in [0, 8): nearest of 0, 0.5, 1, 1.5, 2,
+// 3, 4, 6, ties to the even code.  The thresholds are the midpoints between
+// neighbours; at a midpoint the comparison is strict when the lower
+// neighbour's code is even (0.25, 1.25, 2.5, 5) and not strict when the upper
+// one's is (0.75, 1.75, 3.5).
+__device__ __forceinline__ uint32_t e2m1_magnitude_code(float a) {
+  return (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
+         (a > 5.0f);
+}
+
+__global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const uint16_t* __restrict__ w,
+                                                             long nblocks,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
+  for (long b = (long)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks;
+       b += (long)gridDim.x * blockDim.x) {
+    float v[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(w + b * 32 + c * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[c * 8 + 2 * i] = __uint_as_float(q[i] << 16);
+        v[c * 8 + 2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    int e = -127;
+    if (amax > 0.f) {
+      int ex;
+      (void)frexpf(amax, &ex);  // amax = m 2^ex, 0.5 <= m < 1
+      e = min(max(ex - 1 - 2, -127), 127);
+    }
+    u32x4 out;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = v[d * 8 + i];
+        const uint32_t mag = e2m1_magnitude_code(ldexpf(fabsf(x), -e));
+        const uint32_t code = mag | ((x < 0.f && mag) ? 8u : 0u);
+        word |= code << (4 * i);
+      }
+      out[d] = word;
+    }
+    *reinterpret_cast<u32x4*>(codes + b * 16) = out;
+    scales[b] = static_cast<uint8_t>(e + 127);
+  }
+}
+
+hipError_t mxfp4_quantize(const uint16_t* w, long rows, int cols, uint8_t* codes,
+                          uint8_t* scales, hipStream_t s) {
+  const long nblocks = rows * (cols / 32);
+  if (nblocks <= 0) return hipSuccess;
+  const long grid = std::min<long>((nblocks + 255) / 256, 65536);
+  mxfp4_quantize_kernel<<<grid, 256, 0, s>>>(w, nblocks, codes, scales);
+  return hipGetLastError();
+}
+
+// Eight bf16 weights from one code word (bytes b0..b3, two elements each).
+__device__ __forceinline__ bf16x8 mx_decode8(uint32_t word, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 3);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// 2^(byte - 127) as a float (byte 0 is the subnormal 2^-127).
+__device__ __forceinline__ float mx_scale(uint32_t byte) {
+  return byte ? __uint_as_float(byte << 23) : __uint_as_float(0x00400000u);
+}
+
+// Grouped expert GEMM over the 16-row tiles of the tile list.  Work-group =
+// NW waves on RG*16 weight rows of one expert and one 16-row token tile; the
+// k range is split over the waves (each a multiple of 128), partial sums
+// added in LDS in a fixed order.  Per 128-k step a lane holds RG code blocks
+// (16 bytes each), RG scale bytes and 4 token fragments; two steps in flight.
+template <class P, int NW, int RG>
+__global__ __launch_bounds__(NW * 64) void stream_mx_kernel(P p, const Tile* tiles,
+                                                            const int* ntiles) {
+  __shared__ f32x4 red[NW > 1 ? NW : 1][RG][64];
+  const int nblocks = p.N() / (16 * RG);
+  const int nb = blockIdx.x % nblocks;
+  const int tm = blockIdx.x / nblocks;
+  if (tm >= *ntiles) return;
+  const Tile t = tiles[tm];
+  const int e = t.expert, m0 = t.row0, mcount = t.nrows;
+  const int n0 = nb * (16 * RG);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int kw = p.K() / NW;
+  const int kbeg = w * kw;
+  const int nit = kw / 128;
+
+  const uint8_t* cw[RG];
+  const uint8_t* sw[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    const int row = n0 + g * 16 + r16;
+    cw[g] = p.codes_row(e, row) + kbeg / 2 + q * 16;
+    sw[g] = p.scales_row(e, row) + kbeg / 32 + q;
+  }
+  // token rows past the tile's count read the tile's first row (not stored)
+  const uint16_t* xr = p.a_row(m0 + (r16 < mcount ? r16 : 0)) + kbeg + q * 32;
+
+  f32x4 acc[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 CA[RG], CB[RG];
+  uint32_t SA[RG], SB[RG];
+  bf16x8 XA[4], XB[4];
+  auto load = [&](u32x4(&C)[RG], uint32_t(&S)[RG], bf16x8(&X)[4], int it) {
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      C[g] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cw[g] + it * 64));
+      S[g] = sw[g][it * 4];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) X[u] = load8(xr + it * 128 + u * 8);
+  };
+  auto compute = [&](const u32x4(&C)[RG], const uint32_t(&S)[RG], const bf16x8(&X)[4]) {
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      const float sc = mx_scale(S[g]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[g] = mfma_bf16(mx_decode8(C[g][u], sc), X[u], acc[g]);
+    }
+  };
+  if (nit > 0) load(CA, SA, XA, 0);
+  for (int it = 0; it < nit; it += 2) {
+    if (it + 1 < nit) load(CB, SB, XB, it + 1);
+    compute(CA, SA, XA);
+    if (it + 1 < nit) {
+      if (it + 2 < nit) load(CA, SA, XA, it + 2);
+      compute(CB, SB, XB);
+    }
+  }
+
+  const int ncol = (lane >> 4) * 4;
+  if constexpr (NW == 1) {
+#pragma unroll
+    for (int g = 0; g < RG; ++g)
+      if (r16 < mcount) p.store(e, m0 + r16, n0 + g * 16 + ncol, acc[g]);
+  } else {
+#pragma unroll
+    for (int g = 0; g < RG; ++g) red[w][g][lane] = acc[g];
+    __syncthreads();
+    for (int g = w; g < RG; g += NW) {
+      f32x4 sm = red[0][g][lane];
+#pragma unroll
+      for (int v = 1; v < NW; ++v) sm += red[v][g][lane];
+      if (r16 < mcount) p.store(e, m0 + r16, n0 + g * 16 + ncol, sm);
+    }
+  }
+}
+
+// Waves per work-group: the largest of 4, 2, 1 whose k share is a whole
+// number of 128-k steps (K is a multiple of 128).
+template <class P>
+static hipError_t launch_mx(const P& p, const Tile* tiles, const int* ntiles, int max_tiles,
+                            hipStream_t s) {
+  constexpr int RG = 4;
+  const long grid = (long)max_tiles * (p.N() / (16 * RG));
+  if (grid <= 0) return hipSuccess;
+  if (p.K() % (4 * 128) == 0)
+    stream_mx_kernel<P, 4, RG><<<grid, 256, 0, s>>>(p, tiles, ntiles);
+  else if (p.K() % (2 * 128) == 0)
+    stream_mx_kernel<P, 2, RG><<<grid, 128, 0, s>>>(p, tiles, ntiles);
+  else
+    stream_mx_kernel<P, 1, RG><<<grid, 64, 0, s>>>(p, tiles, ntiles);
+  return hipGetLastError();
+}
+
+hipError_t stream_mx_exp_up(const ExpUpMx& p, const Tile* tiles, const int* ntiles,
+                            int max_tiles, hipStream_t s) {
+  return launch_mx(p, tiles, ntiles, max_tiles, s);
+}
+hipError_t stream_mx_exp_down(const ExpDownMx& p, const Tile* tiles, const int* ntiles,
+                              int max_tiles, hipStream_t s) {
+  return launch_mx(p, tiles, ntiles, max_tiles, s);
+}
+
+}  // namespace lmoe

@@ -100,6 +100,40 @@ def compare(g: GpuRun, x_bits: np.ndarray, hw, sh, rows=None) -> Report:
     )
 
 
+class MxfpExperts:
+    """``obj[e]``: expert e's weights as the oracle quantises them to MXFP4
+    and back (float64), from the bf16 bits of ``src[e]``; cached, with the
+    codes and scales kept for comparison with the GPU quantiser."""
+
+    def __init__(self, src):
+        self.src, self.cache, self.coded = src, {}, {}
+
+    def _make(self, e):
+        codes, scales = O.mxfp4_quantize(self.src[e])
+        self.coded[e] = (codes, scales)
+        self.cache[e] = O.mxfp4_dequantize(codes, scales)
+
+    def prefetch(self, experts, workers=16):
+        from concurrent.futures import ThreadPoolExecutor
+        todo = sorted({int(e) for e in experts} - set(self.cache))
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(self._make, todo))
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self.cache:
+            self._make(e)
+        return self.cache[e]
+
+
+def mxfp4_host_weights(inp, eager_experts=False):
+    """The oracle's view of a layer whose routed experts are stored as MXFP4."""
+    hw = li.HostWeights(inp, eager_experts=eager_experts)
+    hw.expert_up = MxfpExperts(hw.expert_up)
+    hw.expert_down = MxfpExperts(hw.expert_down)
+    return hw
+
+
 def check_properties(g: GpuRun, sh, T: int) -> None:
     """Properties that hold at any size (checked on every token)."""
     K, E = sh.num_experts_per_tok, sh.n_routed_experts

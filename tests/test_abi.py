@@ -28,7 +28,7 @@ def lib():
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lmoe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lmoe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
@@ -121,6 +121,36 @@ def test_create_argument_errors(lib):
     assert st == pkg.LMOE_OK and h.value
     lib.lmoe_destroy(h)
     lib.lmoe_destroy(None)
+
+
+def test_mxfp4_config_weights_and_quantiser_argument_errors(lib):
+    # expert format: a known value, and (MXFP4) latent / expert widths multiple of 128
+    st, _ = create(lib, cfg(expert_format=7))
+    assert st == pkg.LMOE_ERR_INVALID_ARG
+    assert lib.lmoe_workspace_size(ctypes.byref(cfg(expert_format=pkg.EXPERTS_MXFP4))) == 0
+    mx_shape = li.LayerShape(256, 128, 16, 4, 256, 512, 5.0)
+    c = pkg.make_config(mx_shape, 64, expert_format=pkg.EXPERTS_MXFP4)
+    assert lib.lmoe_workspace_size(ctypes.byref(c)) > 0
+    # MXFP4: the code and scale pointers are required (codes 16-byte aligned),
+    # the bf16 expert pointers are not
+    mx = dict(expert_up=None, expert_down=None, expert_up_mxfp4=FAKE, expert_up_scale=FAKE + 1,
+              expert_down_mxfp4=FAKE, expert_down_scale=FAKE + 3)
+    st, h = create(lib, c, weights(**mx))
+    assert st == pkg.LMOE_OK
+    lib.lmoe_destroy(h)
+    for bad in (dict(expert_up_mxfp4=None), dict(expert_down_scale=None),
+                dict(expert_down_mxfp4=FAKE + 8)):
+        assert create(lib, c, weights(**{**mx, **bad}))[0] == pkg.LMOE_ERR_INVALID_ARG
+    # quantiser: cols a positive multiple of 32, rows >= 0, aligned pointers
+    q = lib.lmoe_quantize_mxfp4
+    assert q(FAKE, 4, 48, FAKE, FAKE, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert q(FAKE, 4, 0, FAKE, FAKE, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert q(FAKE, -1, 64, FAKE, FAKE, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert q(FAKE, 0, 64, None, None, None) == pkg.LMOE_OK      # no rows, no launch
+    assert q(None, 4, 64, FAKE, FAKE, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert q(FAKE + 2, 4, 64, FAKE, FAKE, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert q(FAKE, 4, 64, FAKE + 8, FAKE, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert q(FAKE, 4, 64, FAKE, None, None) == pkg.LMOE_ERR_INVALID_ARG
 
 
 def test_forward_and_route_argument_errors(lib):
