@@ -29,12 +29,16 @@ if ROOT not in sys.path:
 METRIC = "LatentMoE layer tokens/s; % HBM roofline (decode) / % bf16 MFMA peak (prefill)"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
-HBM_BOUND = {"tiny", "decode", "mtp_verify", "decode_grouped"}
+HBM_BOUND = {"tiny", "decode", "mtp_verify", "decode_grouped", "decode_mxfp4",
+             "mtp_verify_mxfp4"}
+MXFP4_BYTES = 0.5 + 1.0 / 32
 
 
-def stage_work(sh, T, U):
+def stage_work(sh, T, U, expert_weight_bytes=2.0):
     """Algorithmic bytes and flops of each stage for T tokens touching U
-    distinct experts (weights read once, activations read/written once)."""
+    distinct experts (weights read once, activations read/written once);
+    expert weights take ``expert_weight_bytes`` per element (2 for bf16,
+    0.5 + 1/32 for MXFP4: half a byte per element plus a scale byte per 32)."""
     D, R, E = sh.hidden_size, sh.moe_latent_size, sh.n_routed_experts
     K, F, S = sh.num_experts_per_tok, sh.moe_intermediate_size, sh.moe_shared_expert_intermediate_size
     slots = T * K
@@ -44,8 +48,8 @@ def stage_work(sh, T, U):
         "router_logits": E * R * 4 + T * R * 4 + T * E * 4,
         "router_select": T * E * 4 + E * 4 + slots * 8,
         "dispatch": slots * 4 * 4 + E * 12,
-        "expert_up": U * F * R * 2 + slots * R * 2 + slots * F * 2,
-        "expert_down": U * R * F * 2 + slots * F * 2 + slots * R * 2,
+        "expert_up": int(U * F * R * expert_weight_bytes) + slots * R * 2 + slots * F * 2,
+        "expert_down": int(U * R * F * expert_weight_bytes) + slots * F * 2 + slots * R * 2,
         "combine": slots * R * 2 + slots * 8 + T * R * 2,
         "proj_out": D * (R + S) * 2 + T * (R + S) * 2 + T * D * 2,
     }
@@ -135,7 +139,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode",
                     choices=["tiny", "decode", "mtp_verify", "prefill", "skewed",
-                             "decode_grouped"])
+                             "decode_grouped", "decode_mxfp4", "mtp_verify_mxfp4"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -151,13 +155,21 @@ def main():
     import sparse_moe_layer_latentmoe_amd as pkg
 
     dev = torch.device("cuda:0")
-    wl = li.workload(args.workload)
+    mxfp4 = args.workload.endswith("_mxfp4")
+    wl = li.workload(args.workload[:-len("_mxfp4")] if mxfp4 else args.workload)
     sh, T = wl.shape, wl.tokens
     inp = li.make_inputs(wl, dev)
     weights = {k: getattr(inp, k) for k in (
         "fc1_latent", "router", "router_bias", "expert_up", "expert_down",
         "fc2_latent", "shared_up", "shared_down")}
-    layer = pkg.LatentMoE(sh, weights, max_tokens=T)
+    if mxfp4:
+        # routed experts stored as MXFP4, quantised by the library's kernel
+        up_c, up_s = pkg.quantize_mxfp4(inp.expert_up)
+        dn_c, dn_s = pkg.quantize_mxfp4(inp.expert_down)
+        weights.update(expert_up=None, expert_down=None, expert_up_mxfp4=up_c,
+                       expert_up_scale=up_s, expert_down_mxfp4=dn_c, expert_down_scale=dn_s)
+    layer = pkg.LatentMoE(sh, weights, max_tokens=T,
+                          expert_format=pkg.EXPERTS_MXFP4 if mxfp4 else pkg.EXPERTS_BF16)
     y = torch.empty_like(inp.x)
     counts = torch.empty(sh.n_routed_experts, dtype=torch.int32, device=dev)
     layer.forward_into(inp.x, y, pkg.Taps(expert_counts=counts))
@@ -193,7 +205,7 @@ def main():
     ms_events = (t3 - t2) * 1e3 / args.steps
     stage_ms = {k: v / max(nf, 1) for k, v in stages.items()}
 
-    sb, sf = stage_work(sh, T, U)
+    sb, sf = stage_work(sh, T, U, MXFP4_BYTES if mxfp4 else 2.0)
     hbm = args.workload in HBM_BOUND
     dom = max(stage_ms, key=stage_ms.get)
     if hbm:
@@ -244,8 +256,10 @@ def main():
                                f"hidden {sh.hidden_size}, latent {sh.moe_latent_size}, "
                                f"{sh.n_routed_experts} experts top-{sh.num_experts_per_tok}, "
                                f"expert MLP {sh.moe_intermediate_size}, shared "
-                               f"{sh.moe_shared_expert_intermediate_size}, bf16 weights, "
-                               f"fp32 router",
+                               f"{sh.moe_shared_expert_intermediate_size}, "
+                               + ("MXFP4 routed-expert weights (decoded to bf16), other "
+                                  "weights bf16" if mxfp4 else "bf16 weights")
+                               + ", fp32 router",
                    "tokens": T, "seed": wl.seed, "unique_experts": U,
                    "empty_experts": empty, "max_violation": round(max_vio, 3),
                    "parallelism": "single GPU"},
@@ -256,7 +270,7 @@ def main():
         "stage_timing": f"{nf} further forwards with per-stage HIP events "
                         f"({ms_events:.4f} ms/step with the events)",
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not mxfp4:
         n = min(args.cpu_sample_tokens, T)
         out["cpu_baseline"] = cpu_baseline(inp, sh, n)
     print(json.dumps(out), flush=True)

@@ -14,12 +14,22 @@
 //             ties to the even code (zero mantissa bit), clamped at 6,
 //             signed unless it rounds to 0.
 //   stream    like the bf16 weight-streaming GEMM, with one lane loading the
-//             16 code bytes of one block (32 k of one row) plus its scale
-//             byte: the four lanes of a row cover 128 consecutive k, and MFMA
-//             step u takes code bytes 4u..4u+3 of every lane, converted with
+//             16 code bytes of one block (32 k of one row): the four lanes of
+//             a row cover 128 consecutive k, and MFMA step u takes code bytes
+//             4u..4u+3 of every lane, converted with
 //             v_cvt_scalef32_pk_bf16_fp4 (element 0 = low nibble, measured).
 //             The token fragments are loaded at the same k, so both MFMA
 //             operands agree on which 32 k a step sums over.
+//
+// Streaming the codes at HBM speed is limited by the number of vector-memory
+// instructions, not by bytes or arithmetic: a 16-byte code load carries 32
+// weights, so per code byte the token-fragment and scale loads weigh four
+// times more than in the bf16 kernel.  The main kernel therefore (a) loads
+// both 64-byte halves of every 128-byte code line back to back (the two
+// halves in separate steps let the line leave the cache in between, and the
+// HBM traffic nearly doubles), (b) loads the scales of two 256-k stages with
+// one 16-byte load per row, and (c) splits a work-group's waves over rows,
+// not k, so the token tile is read once per work-group into LDS and shared.
 #include <algorithm>
 
 #include "gemm_problems.h"
@@ -109,11 +119,12 @@ __device__ __forceinline__ float mx_scale(uint32_t byte) {
   return byte ? __uint_as_float(byte << 23) : __uint_as_float(0x00400000u);
 }
 
-// Grouped expert GEMM over the 16-row tiles of the tile list.  Work-group =
-// NW waves on RG*16 weight rows of one expert and one 16-row token tile; the
-// k range is split over the waves (each a multiple of 128), partial sums
-// added in LDS in a fixed order.  Per 128-k step a lane holds RG code blocks
-// (16 bytes each), RG scale bytes and 4 token fragments; two steps in flight.
+// General grouped expert GEMM over the 16-row tiles of the tile list (any K
+// that is a multiple of 128).  Work-group = NW waves on RG*16 weight rows of
+// one expert and one 16-row token tile; the k range is split over the waves
+// (each a multiple of 128), partial sums added in LDS in a fixed order.  Per
+// 128-k step a lane holds RG code blocks (16 bytes each), RG scale bytes and
+// 4 token fragments; two steps in flight.
 template <class P, int NW, int RG>
 __global__ __launch_bounds__(NW * 64) void stream_mx_kernel(P p, const Tile* tiles,
                                                             const int* ntiles) {
@@ -153,7 +164,7 @@ __global__ __launch_bounds__(NW * 64) void stream_mx_kernel(P p, const Tile* til
   auto load = [&](u32x4(&C)[RG], uint32_t(&S)[RG], bf16x8(&X)[4], int it) {
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
-      C[g] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cw[g] + it * 64));
+      C[g] = *reinterpret_cast<const u32x4*>(cw[g] + it * 64);
       S[g] = sw[g][it * 4];
     }
 #pragma unroll
@@ -195,11 +206,151 @@ __global__ __launch_bounds__(NW * 64) void stream_mx_kernel(P p, const Tile* til
   }
 }
 
-// Waves per work-group: the largest of 4, 2, 1 whose k share is a whole
-// number of 128-k steps (K is a multiple of 128).
+// Grouped expert GEMM for K a multiple of 512 (codes and scales 16-byte
+// aligned, N a multiple of WPG*RG*16).  Work-group = WPG waves on one 16-row
+// token tile, wave w on its own RG*16 weight rows over the whole k range (no
+// reduction).  k runs in 256-k stages: per stage a lane loads RG x 2 code
+// blocks (the two halves of each code line together) and reads its 4 x 2 token
+// fragments from LDS; the stage's token tile (16 rows x 256 k) is copied into
+// LDS by the whole work-group one stage ahead (double buffer, one barrier per
+// stage), and the scales come one 16-byte load per row for a pair of stages,
+// one pair ahead.  Work items (tile, row block) are taken XCD-major.
+template <class P, int RG, int WPG>
+__global__ __launch_bounds__(WPG * 64) void stream_mx_shared_kernel(P p, const Tile* tiles,
+                                                                    const int* ntiles) {
+  constexpr int XROW = 256 + 8;         // bf16 per LDS token row (16-byte pad: no bank conflicts)
+  constexpr int XP = 512 / (WPG * 64);  // 16-byte pieces of a stage's token tile per thread
+  static_assert(XP >= 1 && XP * WPG * 64 == 512, "WPG must divide 8");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][16 * XROW];
+
+  // Consecutive blocks go to the 8 XCDs in turn; block b runs work item
+  // (b % 8) * (n / 8) + b / 8 so that the items of one tile (consecutive)
+  // share an XCD and its L2.  Only the live tiles' items are numbered.
+  const int nwg = p.N() / (WPG * 16 * RG);
+  const int nwork = *ntiles * nwg;
+  const int b = blockIdx.x;
+  if (b >= nwork) return;
+  const int per = nwork >> 3;
+  const int item = b < (per << 3) ? (b & 7) * per + (b >> 3) : b;
+  const int nb = item % nwg;
+  const Tile t = tiles[item / nwg];
+  const int e = t.expert, m0 = t.row0, mcount = t.nrows;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int nst = p.K() / 256;  // even
+  const int n0 = (nb * WPG + w) * (16 * RG);
+
+  const uint8_t* cw[RG];
+  const uint8_t* sw[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) {
+    const int row = n0 + g * 16 + r16;
+    cw[g] = p.codes_row(e, row) + q * 16;
+    sw[g] = p.scales_row(e, row);
+  }
+  // token rows past the tile's count copy the tile's first row (not stored)
+  const uint16_t* xsrc[XP];
+  int xdst[XP];
+#pragma unroll
+  for (int j = 0; j < XP; ++j) {
+    const int piece = j * WPG * 64 + threadIdx.x;
+    const int row = piece >> 5, col = (piece & 31) * 8;
+    xsrc[j] = p.a_row(m0 + (row < mcount ? row : 0)) + col;
+    xdst[j] = row * XROW + col;
+  }
+  const int xrd = r16 * XROW + q * 32;
+
+  f32x4 acc[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 CA[2][RG], CB[2][RG];  // code blocks of two stages, [half][row group]
+  u32x4 S0[RG], S1[RG];        // scale bytes of the current and the next stage pair
+  bf16x8 XG[XP];               // token pieces on their way to LDS
+  auto load_codes = [&](u32x4(&C)[2][RG], int st) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int g = 0; g < RG; ++g)
+        C[h][g] = *reinterpret_cast<const u32x4*>(cw[g] + st * 128 + h * 64);
+  };
+  auto load_scales = [&](u32x4(&S)[RG], int st) {
+#pragma unroll
+    for (int g = 0; g < RG; ++g) S[g] = *reinterpret_cast<const u32x4*>(sw[g] + st * 8);
+  };
+  auto load_tokens = [&](int st) {
+#pragma unroll
+    for (int j = 0; j < XP; ++j) XG[j] = load8(xsrc[j] + st * 256);
+  };
+  auto store_tokens = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < XP; ++j) *reinterpret_cast<bf16x8*>(&xs[buf][xdst[j]]) = XG[j];
+  };
+  // one stage: scale byte q of dword 2*odd + h is the scale of this lane's
+  // block in half h of the stage
+  auto compute = [&](const u32x4(&C)[2][RG], int buf, int odd) {
+    bf16x8 X[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        X[h][u] = *reinterpret_cast<const bf16x8*>(&xs[buf][xrd + h * 128 + u * 8]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        const float sc = mx_scale(__builtin_amdgcn_ubfe(S0[g][odd * 2 + h], q * 8, 8));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[g] = mfma_bf16(mx_decode8(C[h][g][u], sc), X[h][u], acc[g]);
+      }
+  };
+
+  load_tokens(0);
+  load_codes(CA, 0);
+  load_scales(S0, 0);
+  store_tokens(0);
+  load_tokens(1);
+  __syncthreads();
+  for (int st = 0; st < nst; st += 2) {
+    const bool more = st + 2 < nst;
+    load_codes(CB, st + 1);
+    if (more) load_scales(S1, st + 2);
+    compute(CA, 0, 0);
+    store_tokens(1);
+    if (more) load_tokens(st + 2);
+    __syncthreads();
+    if (more) load_codes(CA, st + 2);
+    compute(CB, 1, 1);
+    if (more) {
+      store_tokens(0);
+      load_tokens(st + 3);
+#pragma unroll
+      for (int g = 0; g < RG; ++g) S0[g] = S1[g];
+    }
+    __syncthreads();
+  }
+
+  const int ncol = q * 4;
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+    if (r16 < mcount) p.store(e, m0 + r16, n0 + g * 16 + ncol, acc[g]);
+}
+
+// The shared-token kernel where its conditions hold; otherwise the general
+// kernel with the largest of 4, 2, 1 waves per work-group whose k share is a
+// whole number of 128-k steps (K is a multiple of 128).
 template <class P>
 static hipError_t launch_mx(const P& p, const Tile* tiles, const int* ntiles, int max_tiles,
                             hipStream_t s) {
+  constexpr int kSharedRG = 2, kSharedWPG = 8;
+  const bool aligned = ((reinterpret_cast<uintptr_t>(p.codes) | reinterpret_cast<uintptr_t>(p.scales)) & 15) == 0;
+  if (p.K() % 512 == 0 && p.N() % (kSharedWPG * 16 * kSharedRG) == 0 && aligned) {
+    const long grid = (long)max_tiles * (p.N() / (kSharedWPG * 16 * kSharedRG));
+    if (grid <= 0) return hipSuccess;
+    stream_mx_shared_kernel<P, kSharedRG, kSharedWPG><<<grid, kSharedWPG * 64, 0, s>>>(p, tiles, ntiles);
+    return hipGetLastError();
+  }
   constexpr int RG = 4;
   const long grid = (long)max_tiles * (p.N() / (16 * RG));
   if (grid <= 0) return hipSuccess;

@@ -19,6 +19,9 @@ from oracle import lmoe_oracle as O
 pytestmark = pytest.mark.gpu
 
 MX_SMALL = li.LayerShape(256, 128, 16, 4, 256, 512, 5.0)
+# latent and expert widths multiples of 512: both expert GEMMs take the
+# shared-token kernel (MX_SMALL takes the general one, MEDIUM one of each)
+MX_WIDE = li.LayerShape(512, 512, 16, 4, 1024, 512, 5.0)
 
 
 @pytest.fixture(scope="module")
@@ -87,7 +90,8 @@ def mx_weights(inp):
 
 
 @pytest.mark.parametrize("shape,tokens", [(MX_SMALL, 64), (MX_SMALL, 1), (MX_SMALL, 37),
-                                          (MEDIUM, 129), (MEDIUM, 300)])
+                                          (MX_WIDE, 1), (MX_WIDE, 37), (MX_WIDE, 64),
+                                          (MX_WIDE, 200), (MEDIUM, 129), (MEDIUM, 300)])
 def test_mxfp4_forward_matches_oracle(dev, shape, tokens):
     wl = li.Workload("mxfp4", shape, tokens)
     say(f"[mxfp4 forward E={shape.n_routed_experts} R={shape.moe_latent_size} "
