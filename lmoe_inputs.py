@@ -7,13 +7,15 @@ produces; the HIP side gets device tensors, the oracle gets host copies of
 the very same values (bfloat16 bit patterns as uint16, float32 as float32).
 
 Recipe (each tensor has its own generator, seeded ``seed + i`` in the order
-x, W1, Wg, beta, Wup, Wdn, W2, Wsu, Wsd):
+x, W1, Wg, beta, Wup, Wdn, W2, Wsu, Wsd, and gamma, the weight of the block's
+pre-norm, which only the block-boundary runs use):
 
 * x ~ N(0, 1); every weight ~ N(0, 0.02^2); beta ~ N(0, 0.01^2)
   (the second parameter is a variance: standard deviations 1, 0.02, 0.01);
 * draws are float32, then rounded to bfloat16 (round-to-nearest-even) for
   x and every weight except the router gate and its correction bias, which
   stay float32 (the pages keep the gate and the bias in fp32);
+* gamma = 1 + N(0, 0.1^2) per hidden unit, rounded to bfloat16;
 * the "skewed" workload replaces beta by a bias that makes expert
   popularity follow a Zipf law (see ``zipf_bias``).
 
@@ -189,6 +191,13 @@ def make_weights(wl: Workload, device="cpu") -> dict:
     w["shared_down"] = _normal_bf16((D, S), ws, _gen(device, seed + 8), device,
                                     chunk_rows=2048)
     return w
+
+
+def make_norm_weight(wl: Workload, device="cpu") -> torch.Tensor:
+    """gamma [D] bf16: the weight of the block's pre-norm RMSNorm."""
+    g = torch.randn((wl.shape.hidden_size,), generator=_gen(device, wl.seed + 9),
+                    device=device, dtype=torch.float32)
+    return (1.0 + 0.1 * g).to(torch.bfloat16)
 
 
 def make_x(wl: Workload, device="cpu", tokens: int | None = None) -> torch.Tensor:

@@ -36,6 +36,13 @@ Readings taken where the pages are silent or disagree:
   biased scores, equal group scores go to the lower group index, and experts
   of the dropped groups are excluded from the top-K (not given a score of
   zero); with n_group = 1 the group step is a no-op.
+* the block around the layer (``block_forward``; the same page, CH9 §9.3: each
+  block applies a pre-norm RMSNorm, then the mixer, then adds the residual):
+  RMSNorm(h) = gamma * h / sqrt(mean(h^2) + eps) with eps = 1e-5 unless
+  given (the pages give no eps); the product gamma * h is rounded once to
+  bfloat16 (it is the GEMM operand) and the per-token factor
+  1 / sqrt(mean(h^2) + eps) is kept exact, so the normalised input is
+  r_t * bf16(gamma * h_t); the block output is h + layer(RMSNorm(h)).
 
 Parity pins (tests/test_oracle_pins.py): a hand-derived micro example
 (tests/golden/worked_example_micro.json), brute-force subset enumeration for
@@ -44,7 +51,10 @@ the top-K, closed-form sigmoid values, exact integer GEMMs, the dense
 K = 1, K = E, x = 0, Wup = 0, identical experts, token-order equivariance and
 the page's parameter/FLOP accounting; the MXFP4 quantiser by hand-worked
 blocks (ties, saturation, zero blocks), exact round trips and its error
-bound.  No function here is unpinned.
+bound; the pre-norm by hand-worked rounding cases, the unit RMS of its
+output, power-of-two scale invariance, and the block forward against the
+plain forward on inputs that the norm maps exactly.  No function here is
+unpinned.
 """
 
 from __future__ import annotations
@@ -80,6 +90,30 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     float32 whose high half is ``bits`` and whose low half is zero."""
     u = np.asarray(bits, dtype=np.uint16)
     return (u.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(F64)
+
+
+def f32_to_bf16_bits(v) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of float32 values, rounded to nearest
+    with ties to the even pattern (finite inputs)."""
+    u = np.asarray(v, F32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def rms_prenorm(h_bits, gamma_bits, eps: float = 1e-5):
+    """The block's pre-norm RMSNorm (page "Nemotron 3 Ultra 架构深度拆解报告",
+    CH9 §9.3: NemotronHRMSNorm before the mixer; one weight per hidden unit,
+    §2.3.6), split into the GEMM operand and a per-token factor:
+
+        xt_t = bf16(gamma * h_t)      the float32 product, rounded once
+        r_t  = 1 / sqrt(mean_i h_t,i^2 + eps)        (float64)
+
+    so that RMSNorm(h)_t = r_t * xt_t.  Returns (xt bits uint16 [T, D],
+    r float64 [T])."""
+    h = bf16_bits_to_f64(h_bits)
+    g = bf16_bits_to_f64(gamma_bits)
+    xt = f32_to_bf16_bits((h * g[None, :]).astype(F32))
+    r = 1.0 / np.sqrt((h * h).mean(axis=1) + float(eps))
+    return xt, r
 
 
 # Magnitudes of the E2M1 (FP4) element format, by code 0..7 (page "Nemotron 3
@@ -273,8 +307,13 @@ def forward(x_bits, weights, cfg: OracleConfig, forced_idx=None) -> dict:
     expert id).  ``forced_idx`` ([T, K] ascending ids) replaces the
     selection; it is used to re-evaluate tokens whose selection is within
     rounding of a tie.  Returns y (float64) and the intermediate values."""
+    return layer(bf16_bits_to_f64(x_bits), weights, cfg, forced_idx)
+
+
+def layer(x: np.ndarray, weights, cfg: OracleConfig, forced_idx=None) -> dict:
+    """The layer (Steps 1-7) on a float64 input [T, D]; see ``forward``."""
     k = cfg.num_experts_per_tok
-    x = bf16_bits_to_f64(x_bits)
+    x = np.asarray(x, F64)
     z = latent_projection(x, bf16_bits_to_f64(weights.fc1_latent))
     z32 = z.astype(F32)
     logits, s = router_scores(z32, weights.router)
@@ -290,3 +329,20 @@ def forward(x_bits, weights, cfg: OracleConfig, forced_idx=None) -> dict:
     return dict(y=y_routed + y_shared, y_routed=y_routed, y_shared=y_shared,
                 z=z, z32=z32, logits=logits, s=s, b=b, idx=idx, w=w, gap=gap,
                 r=r, counts=counts)
+
+
+def block_forward(h_bits, gamma_bits, weights, cfg: OracleConfig, eps: float = 1e-5,
+                  residual: bool = True, forced_idx=None) -> dict:
+    """The layer inside its block (CH9 §9.3): pre-norm RMSNorm of the residual
+    stream h (bf16 bits [T, D]) with weight ``gamma_bits`` (bf16 bits [D]),
+    the layer on the normalised rows r_t * bf16(gamma * h_t), and, if
+    ``residual``, the residual added: y = h + layer(RMSNorm(h)).  Returns the
+    layer's values with y replaced by the block output, plus xt and rnorm
+    (``rms_prenorm``) and y_layer (the layer's own output)."""
+    xt, rn = rms_prenorm(h_bits, gamma_bits, eps)
+    out = layer(rn[:, None] * bf16_bits_to_f64(xt), weights, cfg, forced_idx)
+    out["y_layer"] = out["y"]
+    if residual:
+        out["y"] = bf16_bits_to_f64(h_bits) + out["y_layer"]
+    out["xt"], out["rnorm"] = xt, rn
+    return out

@@ -509,3 +509,97 @@ def test_tiny_generator_is_seeded():
     assert torch.equal(a.x, b.x) and torch.equal(a.expert_down, b.expert_down)
     assert a.x.dtype == torch.bfloat16 and a.router.dtype == torch.float32
     assert a.expert_up.shape == (16, 128, 64) and a.expert_down.shape == (16, 64, 128)
+
+
+# ---- the block's pre-norm RMSNorm and residual (Ultra teardown CH9 §9.3) ----
+
+def _prenorm_worked():
+    """By hand (D = 4): gamma * h = 1.5 * 1.0078125 = 1.51171875 lies exactly
+    half-way between the bf16 neighbours 1.5078125 and 1.515625 and goes to
+    the even pattern 1.515625; 1.25 * 1.0078125 = 1.259765625 is below the
+    half-way point of 1.2578125 and 1.265625 and rounds down; -1.51171875
+    rounds like its magnitude; 2 * -4 = -8 is exact.  mean(h^2) =
+    (3 * 1.0078125^2 + 16) / 4, r = 1 / sqrt(mean + eps)."""
+    h = exact_bf16_bits([[1.0078125, 1.0078125, -1.0078125, -4.0]])
+    g = exact_bf16_bits([1.5, 1.25, 1.5, 2.0])
+    want_xt = [1.515625, 1.2578125, -1.515625, -8.0]
+    mean = (3 * 1.0078125 ** 2 + 16.0) / 4
+    return h, g, want_xt, mean
+
+
+def test_prenorm_worked_rounding_and_factor():
+    h, g, want_xt, mean = _prenorm_worked()
+    for eps in (0.0, 1e-5, 0.25):
+        xt, r = O.rms_prenorm(h, g, eps)
+        assert O.bf16_bits_to_f64(xt)[0].tolist() == want_xt
+        assert r[0] == pytest.approx(1.0 / math.sqrt(mean + eps), rel=1e-15)
+
+
+def test_prenorm_unit_rms_and_eps_closed_form():
+    rng = np.random.default_rng(7)
+    h = li.bf16_bits(torch.from_numpy(rng.standard_normal((5, 96)).astype(np.float32)).to(torch.bfloat16))
+    ones = exact_bf16_bits(np.ones(96))
+    xt, r = O.rms_prenorm(h, ones, 0.0)
+    assert np.array_equal(xt, h)                   # gamma = 1: the operand is h itself
+    rms = np.sqrt(((r[:, None] * O.bf16_bits_to_f64(xt)) ** 2).mean(1))
+    np.testing.assert_allclose(rms, 1.0, rtol=1e-14)
+    # constant rows c: r = 1 / sqrt(c^2 + eps)
+    c = np.array([0.5, 3.0, -2.0])
+    hc = exact_bf16_bits(np.repeat(c[:, None], 96, 1))
+    _, r = O.rms_prenorm(hc, ones, 0.75)
+    np.testing.assert_allclose(r, 1.0 / np.sqrt(c ** 2 + 0.75), rtol=1e-15)
+
+
+def test_prenorm_power_of_two_scale_invariance():
+    rng = np.random.default_rng(8)
+    h = li.bf16_bits(torch.from_numpy(rng.standard_normal((4, 64)).astype(np.float32)).to(torch.bfloat16))
+    g = li.bf16_bits(torch.from_numpy((1 + 0.1 * rng.standard_normal(64)).astype(np.float32)).to(torch.bfloat16))
+    xt, r = O.rms_prenorm(h, g, 0.0)
+    base = r[:, None] * O.bf16_bits_to_f64(xt)
+    for k in (-3, 2, 5):
+        hk = exact_bf16_bits(O.bf16_bits_to_f64(h) * 2.0 ** k)
+        xk, rk = O.rms_prenorm(hk, g, 0.0)
+        assert np.array_equal(rk[:, None] * O.bf16_bits_to_f64(xk), base)
+
+
+def test_block_forward_is_the_plain_forward_where_the_norm_is_exact():
+    """h = +-2 everywhere: mean(h^2) = 4, so with eps = 0 r = 1/2 and
+    bf16(gamma * h) = +-2 gamma exactly; the normalised rows are +-gamma,
+    which bf16 holds.  The block output must be h plus the plain forward's
+    output on those rows, bit for bit."""
+    x, w, cfg = tiny_inputs()
+    rng = np.random.default_rng(9)
+    T, D = x.shape
+    sign = rng.choice([-1.0, 1.0], size=(T, D))
+    h = exact_bf16_bits(2.0 * sign)
+    g = li.bf16_bits(torch.from_numpy((1 + 0.1 * rng.standard_normal(D)).astype(np.float32)).to(torch.bfloat16))
+    plain = O.forward(exact_bf16_bits(sign * O.bf16_bits_to_f64(g)[None, :]), w, cfg)
+    blk = O.block_forward(h, g, w, cfg, eps=0.0)
+    assert np.all(blk["rnorm"] == 0.5)
+    np.testing.assert_array_equal(blk["idx"], plain["idx"])
+    assert np.array_equal(blk["y"], O.bf16_bits_to_f64(h) + plain["y"])
+    assert np.array_equal(blk["y_layer"], plain["y"])
+    nores = O.block_forward(h, g, w, cfg, eps=0.0, residual=False)
+    assert np.array_equal(nores["y"], plain["y"])
+
+
+def test_planted_prenorm_mistakes_fail_the_pins(monkeypatch):
+    """Sum instead of mean, and truncation instead of round-to-nearest-even:
+    each breaks the worked example."""
+    real = O.rms_prenorm
+
+    def by_sum(h_bits, gamma_bits, eps=1e-5):
+        xt, _ = real(h_bits, gamma_bits, eps)
+        hv = O.bf16_bits_to_f64(h_bits)
+        return xt, 1.0 / np.sqrt((hv * hv).sum(axis=1) + eps)
+
+    def truncated(h_bits, gamma_bits, eps=1e-5):
+        _, r = real(h_bits, gamma_bits, eps)
+        p = (O.bf16_bits_to_f64(h_bits) * O.bf16_bits_to_f64(gamma_bits)[None, :]).astype(np.float32)
+        return (p.view(np.uint32) >> 16).astype(np.uint16), r
+
+    for bad in (by_sum, truncated):
+        monkeypatch.setattr(O, "rms_prenorm", bad)
+        with pytest.raises(AssertionError):
+            test_prenorm_worked_rounding_and_factor()
+    monkeypatch.setattr(O, "rms_prenorm", real)
