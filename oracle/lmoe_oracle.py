@@ -334,15 +334,19 @@ def layer(x: np.ndarray, weights, cfg: OracleConfig, forced_idx=None) -> dict:
 def block_forward(h_bits, gamma_bits, weights, cfg: OracleConfig, eps: float = 1e-5,
                   residual: bool = True, forced_idx=None) -> dict:
     """The layer inside its block (CH9 §9.3): pre-norm RMSNorm of the residual
-    stream h (bf16 bits [T, D]) with weight ``gamma_bits`` (bf16 bits [D]),
-    the layer on the normalised rows r_t * bf16(gamma * h_t), and, if
-    ``residual``, the residual added: y = h + layer(RMSNorm(h)).  Returns the
-    layer's values with y replaced by the block output, plus xt and rnorm
-    (``rms_prenorm``) and y_layer (the layer's own output)."""
-    xt, rn = rms_prenorm(h_bits, gamma_bits, eps)
-    out = layer(rn[:, None] * bf16_bits_to_f64(xt), weights, cfg, forced_idx)
+    stream h (bf16 bits [T, D]) with weight ``gamma_bits`` (bf16 bits [D];
+    None: no pre-norm, the layer reads h), the layer on the normalised rows
+    r_t * bf16(gamma * h_t), and, if ``residual``, the residual added:
+    y = h + layer(RMSNorm(h)).  Returns the layer's values with y replaced by
+    the block output, plus xt and rnorm (``rms_prenorm``; absent without the
+    pre-norm) and y_layer (the layer's own output)."""
+    if gamma_bits is None:
+        out = layer(bf16_bits_to_f64(h_bits), weights, cfg, forced_idx)
+    else:
+        xt, rn = rms_prenorm(h_bits, gamma_bits, eps)
+        out = layer(rn[:, None] * bf16_bits_to_f64(xt), weights, cfg, forced_idx)
+        out["xt"], out["rnorm"] = xt, rn
     out["y_layer"] = out["y"]
     if residual:
         out["y"] = bf16_bits_to_f64(h_bits) + out["y_layer"]
-    out["xt"], out["rnorm"] = xt, rn
     return out

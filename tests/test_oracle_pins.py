@@ -581,6 +581,10 @@ def test_block_forward_is_the_plain_forward_where_the_norm_is_exact():
     assert np.array_equal(blk["y_layer"], plain["y"])
     nores = O.block_forward(h, g, w, cfg, eps=0.0, residual=False)
     assert np.array_equal(nores["y"], plain["y"])
+    # no pre-norm: the layer reads h itself
+    bare = O.block_forward(h, None, w, cfg)
+    assert np.array_equal(bare["y_layer"], O.forward(h, w, cfg)["y"])
+    assert np.array_equal(bare["y"], O.bf16_bits_to_f64(h) + bare["y_layer"])
 
 
 def test_planted_prenorm_mistakes_fail_the_pins(monkeypatch):
