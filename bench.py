@@ -34,11 +34,14 @@ HBM_BOUND = {"tiny", "decode", "mtp_verify", "decode_grouped", "decode_mxfp4",
 MXFP4_BYTES = 0.5 + 1.0 / 32
 
 
-def stage_work(sh, T, U, expert_weight_bytes=2.0):
+def stage_work(sh, T, U, expert_weight_bytes=2.0, block=False):
     """Algorithmic bytes and flops of each stage for T tokens touching U
     distinct experts (weights read once, activations read/written once);
     expert weights take ``expert_weight_bytes`` per element (2 for bf16,
-    0.5 + 1/32 for MXFP4: half a byte per element plus a scale byte per 32)."""
+    0.5 + 1/32 for MXFP4: half a byte per element plus a scale byte per 32).
+    ``block``: the block's pre-norm (timed inside proj_latent: h and gamma
+    read, bf16(gamma h) and 1/rms written) and residual (h read by proj_out)
+    are fused in."""
     D, R, E = sh.hidden_size, sh.moe_latent_size, sh.n_routed_experts
     K, F, S = sh.num_experts_per_tok, sh.moe_intermediate_size, sh.moe_shared_expert_intermediate_size
     slots = T * K
@@ -53,6 +56,9 @@ def stage_work(sh, T, U, expert_weight_bytes=2.0):
         "combine": slots * R * 2 + slots * 8 + T * R * 2,
         "proj_out": D * (R + S) * 2 + T * (R + S) * 2 + T * D * 2,
     }
+    if block:
+        b["proj_latent"] += T * D * 2 + D * 2 + T * D * 2 + T * 4
+        b["proj_out"] += T * D * 2
     f = {
         "proj_latent": 2 * T * D * R,
         "shared_up": 2 * T * D * S,
@@ -139,7 +145,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode",
                     choices=["tiny", "decode", "mtp_verify", "prefill", "skewed",
-                             "decode_grouped", "decode_mxfp4", "mtp_verify_mxfp4"])
+                             "decode_grouped", "decode_mxfp4", "mtp_verify_mxfp4",
+                             "decode_block", "mtp_verify_block", "prefill_block",
+                             "decode_mxfp4_block"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -155,13 +163,19 @@ def main():
     import sparse_moe_layer_latentmoe_amd as pkg
 
     dev = torch.device("cuda:0")
-    mxfp4 = args.workload.endswith("_mxfp4")
-    wl = li.workload(args.workload[:-len("_mxfp4")] if mxfp4 else args.workload)
+    name = args.workload
+    block = name.endswith("_block")
+    name = name[:-len("_block")] if block else name
+    mxfp4 = name.endswith("_mxfp4")
+    wl = li.workload(name[:-len("_mxfp4")] if mxfp4 else name)
     sh, T = wl.shape, wl.tokens
     inp = li.make_inputs(wl, dev)
     weights = {k: getattr(inp, k) for k in (
         "fc1_latent", "router", "router_bias", "expert_up", "expert_down",
         "fc2_latent", "shared_up", "shared_down")}
+    if block:
+        # the block's pre-norm and residual fused: x is the residual stream
+        weights["norm_weight"] = li.make_norm_weight(wl, dev)
     if mxfp4:
         # routed experts stored as MXFP4, quantised by the library's kernel
         up_c, up_s = pkg.quantize_mxfp4(inp.expert_up)
@@ -169,7 +183,8 @@ def main():
         weights.update(expert_up=None, expert_down=None, expert_up_mxfp4=up_c,
                        expert_up_scale=up_s, expert_down_mxfp4=dn_c, expert_down_scale=dn_s)
     layer = pkg.LatentMoE(sh, weights, max_tokens=T,
-                          expert_format=pkg.EXPERTS_MXFP4 if mxfp4 else pkg.EXPERTS_BF16)
+                          expert_format=pkg.EXPERTS_MXFP4 if mxfp4 else pkg.EXPERTS_BF16,
+                          fuse=pkg.FUSE_BLOCK if block else 0)
     y = torch.empty_like(inp.x)
     counts = torch.empty(sh.n_routed_experts, dtype=torch.int32, device=dev)
     layer.forward_into(inp.x, y, pkg.Taps(expert_counts=counts))
@@ -205,8 +220,8 @@ def main():
     ms_events = (t3 - t2) * 1e3 / args.steps
     stage_ms = {k: v / max(nf, 1) for k, v in stages.items()}
 
-    sb, sf = stage_work(sh, T, U, MXFP4_BYTES if mxfp4 else 2.0)
-    hbm = args.workload in HBM_BOUND
+    sb, sf = stage_work(sh, T, U, MXFP4_BYTES if mxfp4 else 2.0, block)
+    hbm = name in HBM_BOUND
     dom = max(stage_ms, key=stage_ms.get)
     if hbm:
         ach = sb[dom] / (stage_ms[dom] * 1e-3) / 1e9
@@ -259,7 +274,9 @@ def main():
                                f"{sh.moe_shared_expert_intermediate_size}, "
                                + ("MXFP4 routed-expert weights (decoded to bf16), other "
                                   "weights bf16" if mxfp4 else "bf16 weights")
-                               + ", fp32 router",
+                               + ", fp32 router"
+                               + (", block pre-norm RMSNorm and residual add fused"
+                                  if block else ""),
                    "tokens": T, "seed": wl.seed, "unique_experts": U,
                    "empty_experts": empty, "max_violation": round(max_vio, 3),
                    "parallelism": "single GPU"},
@@ -270,7 +287,7 @@ def main():
         "stage_timing": f"{nf} further forwards with per-stage HIP events "
                         f"({ms_events:.4f} ms/step with the events)",
     }
-    if not args.no_cpu_baseline and not mxfp4:
+    if not args.no_cpu_baseline and not mxfp4 and not block:
         n = min(args.cpu_sample_tokens, T)
         out["cpu_baseline"] = cpu_baseline(inp, sh, n)
     print(json.dumps(out), flush=True)

@@ -13,6 +13,19 @@
  *   r    = sum_k w_k relu(z Wup[I_k]^T)^2 Wdn[I_k]^T            [T, R]
  *   y    = r W2^T + relu(x Wsu^T)^2 Wsd^T  fc2_latent + shared   [T, D]
  *
+ * Optionally (lmoe_config.fuse) the layer also takes over the two steps of
+ * its block on either side (page "Nemotron 3 Ultra 架构深度拆解报告", CH9 §9.3:
+ * pre-norm RMSNorm, mixer, residual add); x is then the block's residual
+ * stream h:
+ *
+ *   PRENORM   the layer runs on RMSNorm(h) = r * bf16(gamma * h) with
+ *             r = 1 / sqrt(mean(h^2) + norm_eps) per token: the GEMM operand
+ *             is the bf16 rounding of gamma * h and r scales the fp32 results
+ *             of the latent and shared-up projections (RMSNorm in exact
+ *             arithmetic, one bf16 rounding, placed where it can be
+ *             reproduced exactly);
+ *   RESIDUAL  y = h + (layer output), added in fp32 before the bf16 rounding.
+ *
  * Sizes follow the model's config keys (page "Nemotron-3-Labs-Ultra-Math-SFT"
  * article, 核心配置速查表): D = hidden_size, R = moe_latent_size,
  * E = n_routed_experts, K = num_experts_per_tok, F = moe_intermediate_size,
@@ -73,6 +86,12 @@ typedef enum { LMOE_PATH_AUTO = 0, LMOE_PATH_STREAM = 1, LMOE_PATH_TILED = 2 } l
  * be multiples of 128).  Everything else stays bf16 / fp32. */
 typedef enum { LMOE_EXPERTS_BF16 = 0, LMOE_EXPERTS_MXFP4 = 1 } lmoe_expert_format;
 
+/* Block steps fused into the layer (bits of lmoe_config.fuse; CH9 §9.3 of
+ * the page "Nemotron 3 Ultra 架构深度拆解报告"): the block's pre-norm RMSNorm
+ * (needs lmoe_weights.norm_weight) and its residual add.  See the top of
+ * this file for the exact arithmetic. */
+typedef enum { LMOE_FUSE_PRENORM = 1, LMOE_FUSE_RESIDUAL = 2 } lmoe_fuse;
+
 typedef struct {
   int32_t hidden_size;                         /* D; multiple of 64 */
   int32_t moe_latent_size;                     /* R; multiple of 64 */
@@ -88,6 +107,8 @@ typedef struct {
   int32_t max_tokens;                          /* largest T a forward may use; sizes the workspace */
   int32_t path;                                /* lmoe_path */
   int32_t expert_format;                       /* lmoe_expert_format */
+  int32_t fuse;                                /* lmoe_fuse bits; 0 = the layer alone */
+  float norm_eps;                              /* RMSNorm epsilon, finite, >= 0 (PRENORM) */
 } lmoe_config;
 
 /* Device pointers; the handle borrows them and they must outlive it. */
@@ -105,6 +126,8 @@ typedef struct {
   const uint8_t *expert_up_scale;   /* [E, F, R/32] block scales */
   const uint8_t *expert_down_mxfp4; /* [E, R, F/2] codes, 16-byte aligned */
   const uint8_t *expert_down_scale; /* [E, R, F/32] block scales */
+  /* LMOE_FUSE_PRENORM only (may be NULL otherwise): */
+  const uint16_t *norm_weight;      /* bf16 [D] RMSNorm weight gamma */
 } lmoe_weights;
 
 /* Optional device outputs of intermediate values (tests, monitoring).  Any
@@ -130,7 +153,10 @@ lmoe_status lmoe_create(const lmoe_config *cfg, const lmoe_weights *w, void *wor
                         size_t workspace_bytes, lmoe_handle **out);
 
 /* y = LatentMoE(x) for T tokens.  x: bf16 [T, D], y: bf16 [T, D] (must not
- * overlap x).  T = 0 is a no-op.  `taps` may be NULL.  Page steps 1-7. */
+ * overlap x).  T = 0 is a no-op.  `taps` may be NULL.  Page steps 1-7.
+ * With fuse bits set: x is the residual stream h and y = h + LatentMoE(
+ * RMSNorm(h)) (or either part alone); taps->z_f32 is then the latent of the
+ * normalised input. */
 lmoe_status lmoe_forward(lmoe_handle *h, const uint16_t *x, int32_t T, uint16_t *y,
                          void *stream, const lmoe_taps *taps);
 
@@ -163,7 +189,8 @@ const char *lmoe_status_string(lmoe_status s);
 
 /* Number of timed stages of lmoe_forward and the name of stage i.  Stages
  * 0..7 run back to back on the forward's stream (the last one, proj_out,
- * includes the wait for the auxiliary stream); stage 8 ("shared_up") is
+ * includes the wait for the auxiliary stream; the first, proj_latent,
+ * includes the pre-norm kernel when it is fused); stage 8 ("shared_up") is
  * timed on the auxiliary stream and overlaps the stages before proj_out. */
 int32_t lmoe_num_stages(void);
 const char *lmoe_stage_name(int32_t i);

@@ -28,6 +28,8 @@ LMOE_ERR_HIP = -5
 
 PATH_AUTO, PATH_STREAM, PATH_TILED = 0, 1, 2
 EXPERTS_BF16, EXPERTS_MXFP4 = 0, 1
+FUSE_PRENORM, FUSE_RESIDUAL = 1, 2      # lmoe_fuse bits
+FUSE_BLOCK = FUSE_PRENORM | FUSE_RESIDUAL
 
 EXPORTED = (
     "lmoe_workspace_size", "lmoe_create", "lmoe_forward", "lmoe_route", "lmoe_destroy",
@@ -50,6 +52,8 @@ class LmoeConfig(ctypes.Structure):
         ("max_tokens", ctypes.c_int32),
         ("path", ctypes.c_int32),
         ("expert_format", ctypes.c_int32),
+        ("fuse", ctypes.c_int32),
+        ("norm_eps", ctypes.c_float),
     ]
 
 
@@ -57,7 +61,7 @@ class LmoeWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "fc1_latent", "router", "router_bias", "expert_up", "expert_down",
         "fc2_latent", "shared_up", "shared_down", "expert_up_mxfp4", "expert_up_scale",
-        "expert_down_mxfp4", "expert_down_scale")]
+        "expert_down_mxfp4", "expert_down_scale", "norm_weight")]
 
 
 class LmoeTaps(ctypes.Structure):
@@ -123,14 +127,16 @@ def stage_names() -> list:
 
 
 def make_config(shape, max_tokens: int, path: int = PATH_AUTO,
-                expert_format: int = EXPERTS_BF16) -> LmoeConfig:
+                expert_format: int = EXPERTS_BF16, fuse: int = 0,
+                norm_eps: float = 1e-5) -> LmoeConfig:
     """Config struct from any object with the model's config-key attributes."""
     return LmoeConfig(
         shape.hidden_size, shape.moe_latent_size, shape.n_routed_experts,
         shape.num_experts_per_tok, shape.moe_intermediate_size,
         shape.moe_shared_expert_intermediate_size, int(getattr(shape, "n_group", 1)),
         int(getattr(shape, "topk_group", 1)),
-        float(shape.routed_scaling_factor), int(max_tokens), int(path), int(expert_format))
+        float(shape.routed_scaling_factor), int(max_tokens), int(path), int(expert_format),
+        int(fuse), float(norm_eps))
 
 
 def workspace_size(cfg: LmoeConfig) -> int:
@@ -185,14 +191,17 @@ class LatentMoE:
     ``weights`` maps the lmoe_weights field names to contiguous device
     tensors (bf16, the router and its bias fp32).  The workspace is a
     uint8 device tensor allocated here with torch; the library itself never
-    allocates."""
+    allocates.  ``fuse`` (FUSE_PRENORM | FUSE_RESIDUAL bits) makes the
+    forward take the block's residual stream h and return h + layer(
+    RMSNorm(h)); the pre-norm needs ``weights["norm_weight"]`` (bf16 [D])."""
 
     def __init__(self, shape, weights: dict, max_tokens: int, path: int = PATH_AUTO,
-                 device=None, expert_format: int = EXPERTS_BF16):
+                 device=None, expert_format: int = EXPERTS_BF16, fuse: int = 0,
+                 norm_eps: float = 1e-5):
         import torch
         self.lib = load_library()
         self.shape = shape
-        self.cfg = make_config(shape, max_tokens, path, expert_format)
+        self.cfg = make_config(shape, max_tokens, path, expert_format, fuse, norm_eps)
         ws_bytes = workspace_size(self.cfg)
         if ws_bytes == 0:
             raise LmoeError(LMOE_ERR_UNSUPPORTED, "lmoe_workspace_size")

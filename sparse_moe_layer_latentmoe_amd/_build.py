@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liblmoe.so")
 SOURCES = ["lmoe_api.cpp", "gemm_stream.hip", "gemm_tiled.hip", "router.hip", "dispatch.hip",
-           "mxfp4.hip"]
+           "mxfp4.hip", "block.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

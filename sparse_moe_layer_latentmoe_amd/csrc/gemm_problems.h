@@ -19,7 +19,9 @@ namespace lmoe {
 // fp32 (router input) and bf16 (expert input); n >= R gives the shared
 // expert's hidden relu(.)^2 in bf16.  One launch covers the columns
 // [noff, noff + ncount), so the latent and the shared part can run as two
-// launches on two streams (R is a multiple of every column block).
+// launches on two streams (R is a multiple of every column block).  With the
+// block's pre-norm fused, x holds bf16(gamma * h) and rscale[m] (the token's
+// 1 / rms) multiplies row m's fp32 sums before the epilogue.
 struct ProjIn {
   const uint16_t* x;
   const uint16_t* w1;
@@ -29,6 +31,7 @@ struct ProjIn {
   uint16_t* hs;
   int T, D, R, S;
   int noff, ncount;
+  const float* rscale;  // [T] or null
   static constexpr bool kGatherA = false;
   __device__ const uint16_t* a_base0() const { return x; }
   __device__ const uint16_t* a_base1() const { return x; }
@@ -48,6 +51,7 @@ struct ProjIn {
   __device__ const uint16_t* a_row1(int) const { return nullptr; }
   __device__ void store(int, int m, int n, f32x4 v) const {
     const int g = noff + n;
+    if (rscale) v *= rscale[m];
     if (g < R) {
       *reinterpret_cast<f32x4*>(z32 + (size_t)m * R + g) = v;
       store4_bf16(z16 + (size_t)m * R + g, v);
@@ -60,6 +64,8 @@ struct ProjIn {
 // y = [r | Hs] [W2 | Wsd]^T  (fc2_latent plus the shared expert's down
 // projection, Step 7: the routed and shared outputs are added, so one GEMM
 // over the concatenated k range gives their sum with a single rounding).
+// With the block's residual fused, resid (the block input h, bf16 [T, D]) is
+// added to the fp32 sums before that rounding.
 struct ProjOut {
   const uint16_t* r16;
   const uint16_t* hs;
@@ -67,6 +73,7 @@ struct ProjOut {
   const uint16_t* wsd;
   uint16_t* y;
   int T, D, R, S;
+  const uint16_t* resid;  // [T, D] or null
   static constexpr bool kGatherA = false;
   __device__ const uint16_t* a_base0() const { return r16; }
   __device__ const uint16_t* a_base1() const { return hs; }
@@ -82,6 +89,13 @@ struct ProjOut {
   __device__ const uint16_t* a_row0(int m) const { return r16 + (size_t)m * R; }
   __device__ const uint16_t* a_row1(int m) const { return hs + (size_t)m * S; }
   __device__ void store(int, int m, int n, f32x4 v) const {
+    if (resid) {
+      const u16x4 h = *reinterpret_cast<const u16x4*>(resid + (size_t)m * D + n);
+      v[0] += bf16_to_f32(h[0]);
+      v[1] += bf16_to_f32(h[1]);
+      v[2] += bf16_to_f32(h[2]);
+      v[3] += bf16_to_f32(h[3]);
+    }
     store4_bf16(y + (size_t)m * D + n, v);
   }
 };

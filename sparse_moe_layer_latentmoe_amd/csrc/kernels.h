@@ -77,6 +77,11 @@ hipError_t dispatch(const int32_t* idx, int T, int K, int E, int32_t* blockcnt, 
                     int32_t* offsets, int32_t* rows_tok, int32_t* inv, Tile* tiles,
                     int32_t* ntiles, int tile_m, hipStream_t s);
 
+// The block's pre-norm for T tokens of width D (a multiple of 8): xt =
+// bf16(gamma * h) [T, D] and rn = 1 / sqrt(mean(h^2) + eps) [T].
+hipError_t prenorm(const uint16_t* h, const uint16_t* gamma, int T, int D, float eps,
+                   uint16_t* xt, float* rn, hipStream_t s);
+
 // r = sum_k w[t][k] O[inv[t][k]] -> r16 (bf16) and, if r32 != NULL, fp32.
 hipError_t combine(const uint16_t* o, const int32_t* inv, const float* w, int T, int K, int R,
                    uint16_t* r16, float* r32, hipStream_t s);

@@ -3,6 +3,7 @@
 //
 // Launch sequence (no host synchronisation; page "Nemotron 3 Ultra 架构深度
 // 拆解报告", CH5 §5.6 Steps 1-7).  On the caller's stream:
+//  [prenorm        h -> bf16(gamma h), 1/rms   (block pre-norm, CH9 §9.3)]
 //   proj_latent    x -> z (fp32 + bf16)                        (Step 5)
 //   router_logits  z (fp32) -> logits                          (Step 1)
 //   router_select  logits -> top-K experts and weights         (Steps 2-4)
@@ -10,7 +11,7 @@
 //   expert_up      relu(z16 Wup[e]^T)^2                        (Step 6)
 //   expert_down    H Wdn[e]^T                                  (Step 6)
 //   combine        r = sum_k w O                               (Step 6 index_add_)
-//   proj_out       y = r W2^T + Hs Wsd^T                       (Step 7)
+//   proj_out       y = r W2^T + Hs Wsd^T  [+ h, block residual] (Step 7)
 // and, forked onto the handle's auxiliary stream (before proj_latent for
 // weight-streaming batches, after it otherwise) and joined before proj_out
 // (the shared expert only needs x):
@@ -85,6 +86,10 @@ lmoe_status check_config(const lmoe_config* c) {
   if (c->expert_format == LMOE_EXPERTS_MXFP4 &&
       (c->moe_latent_size % 128 || c->moe_intermediate_size % 128))
     return LMOE_ERR_UNSUPPORTED;
+  // block steps: known bits; the pre-norm's epsilon finite and >= 0
+  if (c->fuse & ~(LMOE_FUSE_PRENORM | LMOE_FUSE_RESIDUAL)) return LMOE_ERR_INVALID_ARG;
+  if ((c->fuse & LMOE_FUSE_PRENORM) && !(std::isfinite(c->norm_eps) && c->norm_eps >= 0.f))
+    return LMOE_ERR_INVALID_ARG;
   if (c->max_tokens > (1 << 22)) return LMOE_ERR_UNSUPPORTED;
   if (c->path == LMOE_PATH_TILED && !tiled_dims_ok(*c)) return LMOE_ERR_UNSUPPORTED;
   return LMOE_OK;
@@ -97,8 +102,8 @@ long max_tiles(const lmoe_config& c, long T, int tile_m) {
 }
 
 struct Layout {
-  size_t z32, z16, hs, part, logits, idx, tw, counts, offsets, blockcnt, rows_tok, inv, tiles, ntiles,
-      h, o, r16, total;
+  size_t xt, rn, z32, z16, hs, part, logits, idx, tw, counts, offsets, blockcnt, rows_tok, inv,
+      tiles, ntiles, h, o, r16, total;
 };
 
 Layout make_layout(const lmoe_config& c) {
@@ -113,6 +118,9 @@ Layout make_layout(const lmoe_config& c) {
     off = align_up(off + bytes, 256);
     return at;
   };
+  const bool prenorm_fused = (c.fuse & LMOE_FUSE_PRENORM) != 0;
+  L.xt = take(prenorm_fused ? T * c.hidden_size * 2 : 0);
+  L.rn = take(prenorm_fused ? T * 4 : 0);
   L.z32 = take(T * R * 4);
   L.z16 = take(T * R * 2);
   L.hs = take(T * S * 2);
@@ -189,6 +197,8 @@ lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, void* wor
              !aligned16(w->expert_down)) {
     return LMOE_ERR_INVALID_ARG;
   }
+  if ((cfg->fuse & LMOE_FUSE_PRENORM) && (!w->norm_weight || !aligned16(w->norm_weight)))
+    return LMOE_ERR_INVALID_ARG;
   const Layout L = make_layout(*cfg);
   if (!workspace || workspace_bytes < L.total) return LMOE_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return LMOE_ERR_WORKSPACE;
@@ -345,6 +355,13 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   const int tile_m = expert_tiled ? tiled_block_m() : kStreamTileM;
   const int ntile_max = static_cast<int>(max_tiles(c, T, tile_m));
 
+  // Block pre-norm: the projections read bf16(gamma h) and scale by 1/rms.
+  const bool prenorm_fused = (c.fuse & LMOE_FUSE_PRENORM) != 0;
+  uint16_t* xt = h->at<uint16_t>(h->L.xt);
+  float* rn = h->at<float>(h->L.rn);
+  const uint16_t* xin = prenorm_fused ? xt : x;
+  const float* rscale = prenorm_fused ? rn : nullptr;
+  const uint16_t* resid = (c.fuse & LMOE_FUSE_RESIDUAL) ? x : nullptr;
   float* z32 = h->at<float>(h->L.z32);
   uint16_t* z16 = h->at<uint16_t>(h->L.z16);
   uint16_t* hs = h->at<uint16_t>(h->L.hs);
@@ -399,7 +416,7 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
     if (!ok(hipEventRecord(h->fork, s)) || !ok(hipStreamWaitEvent(h->aux, h->fork, 0)))
       return false;
     if (ev && !ok(hipEventRecord(ev[kMainStages + 1], h->aux))) return false;
-    ProjIn pshared{x, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, R, S};
+    ProjIn pshared{xin, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, R, S, rscale};
     if (!ok(proj_in(pshared, h->aux))) return false;
     if (ev && !ok(hipEventRecord(ev[kMainStages + 2], h->aux))) return false;
     return ok(hipEventRecord(h->join, h->aux));
@@ -409,9 +426,11 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   // after the latent projection (the split-k path's partial sums are one
   // buffer, and the tiled GEMMs would only compete for the same CUs).
   const bool fork_first = dense == Dense::kStream;
-  if (fork_first && !fork_shared()) return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
-  ProjIn platent{x, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, 0, R};
+  if (prenorm_fused && !ok(prenorm(x, h->w.norm_weight, T, D, c.norm_eps, xt, rn, s)))
+    return LMOE_ERR_HIP;
+  if (fork_first && !fork_shared()) return LMOE_ERR_HIP;
+  ProjIn platent{xin, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, 0, R, rscale};
   if (!ok(proj_in(platent, s))) return LMOE_ERR_HIP;
   if (!fork_first && !fork_shared()) return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
@@ -448,9 +467,9 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   if (!ok(combine(O, inv, tw, T, K, R, r16, taps ? taps->r_latent : nullptr, s)))
     return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
-  // join, then y = r W2^T + Hs Wsd^T
+  // join, then y = r W2^T + Hs Wsd^T (+ h with the block residual fused)
   if (!ok(hipStreamWaitEvent(s, h->join, 0))) return LMOE_ERR_HIP;
-  ProjOut pout{r16, hs, h->w.fc2_latent, h->w.shared_down, y, T, D, R, S};
+  ProjOut pout{r16, hs, h->w.fc2_latent, h->w.shared_down, y, T, D, R, S, resid};
   if (!ok(proj_out(pout, s))) return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
 

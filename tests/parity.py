@@ -6,7 +6,12 @@ Bar (stated once here, used by every test):
   gap between the K-th and (K+1)-th biased score is below TIE_GAP (those are
   counted, and the oracle is re-run with the GPU's selection for them);
 * the bf16 output is within OUT_REL of the oracle in normwise max relative
-  error, max|y - y_ref| / max|y_ref|.
+  error, max|y - y_ref| / max|y_ref|;
+* with the block's residual fused (y = bf16(h + layer)), the layer's part
+  y - h is also within OUT_REL of the oracle's layer output, normwise, once
+  each element's error is reduced by the bound of y's own bf16 rounding
+  (2^-8 |y|), which no kernel can avoid and which dominates where |h| is
+  large next to the layer's output.
 """
 
 from __future__ import annotations
@@ -79,24 +84,48 @@ class Report:
     rel_r: float
     rel_z: float
     max_w_err: float
+    rel_layer: float | None = None   # with the residual fused: (y - h) vs the layer's output
 
 
-def compare(g: GpuRun, x_bits: np.ndarray, hw, sh, rows=None) -> Report:
+@dataclass
+class Block:
+    """The block steps fused into a run: the pre-norm weight's bf16 bits
+    (None: no pre-norm), its epsilon, and whether the residual is added."""
+    gamma_bits: np.ndarray | None
+    eps: float
+    residual: bool
+
+
+def oracle_run(x_bits, hw, cfg, block: Block | None, forced_idx=None) -> dict:
+    if block is None:
+        return O.forward(x_bits, hw, cfg, forced_idx=forced_idx)
+    return O.block_forward(x_bits, block.gamma_bits, hw, cfg, block.eps, block.residual,
+                           forced_idx=forced_idx)
+
+
+def compare(g: GpuRun, x_bits: np.ndarray, hw, sh, rows=None, block: Block | None = None) -> Report:
     """Oracle on the rows ``rows`` of the batch (all if None) vs the GPU run."""
     cfg = oracle_config(sh)
     sel = np.arange(x_bits.shape[0]) if rows is None else np.asarray(rows)
-    ref = O.forward(x_bits[sel], hw, cfg)
+    ref = oracle_run(x_bits[sel], hw, cfg, block)
     tie = ref["gap"] < TIE_GAP
     gidx = g.idx[sel]
     mism = int((~np.all(gidx == ref["idx"], axis=1) & ~tie).sum())
-    forced = O.forward(x_bits[sel], hw, cfg, forced_idx=gidx) if (tie.any() or mism) else ref
+    forced = (oracle_run(x_bits[sel], hw, cfg, block, forced_idx=gidx)
+              if (tie.any() or mism) else ref)
     y = g.y.float().cpu().numpy()[sel]
+    rel_layer = None
+    if block is not None and block.residual:
+        yl = np.asarray(forced["y_layer"], np.float64)
+        err = np.abs(y - O.bf16_bits_to_f64(x_bits[sel]) - yl) - 2.0 ** -8 * np.abs(y)
+        rel_layer = float(max(err.max(), 0.0) / max(np.abs(yl).max(), 1e-300))
     return Report(
         ties=int(tie.sum()), mismatched=mism,
         rel_y=normwise_rel(y, forced["y"]),
         rel_r=normwise_rel(g.r[sel], forced["r"]),
         rel_z=normwise_rel(g.z32[sel], ref["z32"]),
         max_w_err=float(np.abs(g.w[sel].astype(np.float64) - forced["w"]).max()),
+        rel_layer=rel_layer,
     )
 
 
@@ -160,6 +189,8 @@ def assert_parity(rep: Report, max_ties=None) -> None:
     assert rep.max_w_err <= 5e-5, rep
     assert rep.rel_r <= OUT_REL, rep
     assert rep.rel_y <= OUT_REL, rep
+    if rep.rel_layer is not None:
+        assert rep.rel_layer <= OUT_REL, rep
 
 
 MEDIUM = li.LayerShape(1024, 256, 32, 6, 512, 1024, 5.0)

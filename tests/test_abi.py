@@ -153,6 +153,31 @@ def test_mxfp4_config_weights_and_quantiser_argument_errors(lib):
     assert q(FAKE, 4, 64, FAKE, None, None) == pkg.LMOE_ERR_INVALID_ARG
 
 
+def test_block_fusion_config_and_weights(lib):
+    # fuse bits: PRENORM (needs a finite eps >= 0 and the norm weight) and RESIDUAL
+    base = lib.lmoe_workspace_size(ctypes.byref(cfg()))
+    pre = lib.lmoe_workspace_size(ctypes.byref(cfg(fuse=pkg.FUSE_BLOCK)))
+    assert pre > base                                       # xt [T, D] and 1/rms [T]
+    assert lib.lmoe_workspace_size(ctypes.byref(cfg(fuse=pkg.FUSE_RESIDUAL))) == base
+    for bad in (dict(fuse=4), dict(fuse=-1), dict(fuse=pkg.FUSE_PRENORM, norm_eps=-1.0),
+                dict(fuse=pkg.FUSE_PRENORM, norm_eps=float("inf")),
+                dict(fuse=pkg.FUSE_PRENORM, norm_eps=float("nan"))):
+        c = cfg(**bad)
+        assert lib.lmoe_workspace_size(ctypes.byref(c)) == 0, bad
+        assert create(lib, c, nbytes=1 << 30)[0] == pkg.LMOE_ERR_INVALID_ARG, bad
+    # a negative eps is fine when the pre-norm is not fused (the field is unused)
+    assert lib.lmoe_workspace_size(ctypes.byref(cfg(fuse=pkg.FUSE_RESIDUAL, norm_eps=-1.0))) > 0
+    c = cfg(fuse=pkg.FUSE_BLOCK, norm_eps=0.0)
+    assert create(lib, c)[0] == pkg.LMOE_ERR_INVALID_ARG             # no norm weight
+    assert create(lib, c, weights(norm_weight=FAKE + 2))[0] == pkg.LMOE_ERR_INVALID_ARG
+    st, h = create(lib, c, weights(norm_weight=FAKE))
+    assert st == pkg.LMOE_OK
+    lib.lmoe_destroy(h)
+    st, h = create(lib, cfg(fuse=pkg.FUSE_RESIDUAL))           # residual alone: no weight needed
+    assert st == pkg.LMOE_OK
+    lib.lmoe_destroy(h)
+
+
 def test_forward_and_route_argument_errors(lib):
     c = cfg()
     st, h = create(lib, c)
