@@ -3,11 +3,11 @@
 //
 // Work-group tile: BM token rows x BN weight rows, k in steps of BK.  Eight
 // waves (2 along tokens x 4 along weights) each own a (BM/2) x (BN/4)
-// sub-tile of MFMA 16x16x32 tiles.  Two waves per SIMD are needed: measured
-// on MI355X, one wave per SIMD issuing independent 16x16x32 bf16 MFMAs back
-// to back tops out near 63% of the matrix-core peak however many
-// accumulators it cycles through (16 to 64), two waves reach ~90%.  That
-// caps a wave at 256 registers and its sub-tile at 64 x 128 accumulators.
+// sub-tile of MFMA 16x16x32 tiles; with two waves per SIMD a wave has 256
+// registers, so its sub-tile is 64 x 128 accumulators.  Four-wave variants
+// with 128 x 128 accumulators per wave (one wave per SIMD, which can keep the
+// matrix cores ~95% busy on its own) were measured and were not faster on the
+// expert GEMMs: their time goes to the global -> LDS stream, not MFMA issue.
 //
 // Operands move global -> LDS with gfx950's direct 16-byte loads
 // (global_load_lds_dwordx4), NS stages in flight and no staging registers;
