@@ -147,7 +147,7 @@ def main():
                     choices=["tiny", "decode", "mtp_verify", "prefill", "skewed",
                              "decode_grouped", "decode_mxfp4", "mtp_verify_mxfp4",
                              "decode_block", "mtp_verify_block", "prefill_block",
-                             "decode_mxfp4_block"])
+                             "decode_mxfp4_block", "prefill_mxfp4"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()

@@ -21,6 +21,7 @@
 // never spans two experts.
 #include "gemm_problems.h"
 #include "kernels.h"
+#include "mxfp4_device.h"
 
 namespace lmoe {
 
@@ -239,6 +240,156 @@ __global__ __launch_bounds__(128 * WGN) void tiled_gemm_kernel(P p, int mrows, c
     }
 }
 
+// Grouped expert GEMM with MXFP4 weights for large batches: the main loop of
+// tiled_gemm_kernel (NS = 2 stages of 64 k), with each stage's weight rows
+// decoded from FP4 codes instead of copied.  Every lane owns whole 32-k code
+// blocks (16 code bytes and a scale byte each; BN / 256 blocks per stage),
+// loads them into registers two stages ahead, decodes them exactly to bf16
+// and writes them into the stage's swizzled weight rows; the token rows keep
+// the direct global -> LDS copy.  The codes cut the weight bytes moved to a
+// quarter; the MFMA part is unchanged.
+template <class P, int BM, int BN, int WGN>
+__global__ __launch_bounds__(128 * WGN) void tiled_mx_kernel(P p, const Tile* tiles, const int* ntiles) {
+  constexpr int BK = 64, NS = 2;
+  constexpr int NW = 2 * WGN;
+  constexpr int TM = BM / 32, TN = BN / (16 * WGN);
+  constexpr int CPR = BK / 8, RPI = 64 / CPR, RPB = 256 / (BK * 2);
+  constexpr int NIA = BM / RPI / NW;      // token DMA instructions per wave per stage
+  constexpr int NBL = BN / (32 * NW);     // weight blocks (32 k of a row) per lane per stage
+  static_assert(NBL >= 1 && NBL * 32 * NW == BN, "BN");
+  constexpr int NCL = 2 * NBL;            // code + scale loads per lane per stage
+  constexpr int SROWS = BM + BN;
+  static_assert((BM / RPI) % NW == 0, "rows per stage");
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NS][SROWS * BK];
+
+  int tm, nb;
+  if (!work_item<true>(p.N() / BN, 0, BM, tiles, ntiles, tm, nb)) return;
+  const Tile t = tiles[tm];
+  const int e = __builtin_amdgcn_readfirstlane(t.expert);
+  const int m0 = __builtin_amdgcn_readfirstlane(t.row0);
+  const int mcount = __builtin_amdgcn_readfirstlane(t.nrows);
+  const int n0 = nb * BN;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nk = p.K() / BK;
+  auto swz = [](int row) { return (row / RPB) & (CPR - 1); };
+
+  const int lr = lane / CPR;
+  const int chunk8 = ((lane % CPR) ^ swz(RPI * w + lr)) * 8;
+  const uint16_t* pa[NIA];
+#pragma unroll
+  for (int j = 0; j < NIA; ++j) {
+    const int row = RPI * (w + NW * j) + lr;
+    pa[j] = p.a_row(m0 + (row < mcount ? row : 0)) + chunk8;
+  }
+  auto issue_a = [&](int kt) {
+    uint16_t* stage = &smem[kt % NS][0];
+#pragma unroll
+    for (int j = 0; j < NIA; ++j)
+      __builtin_amdgcn_global_load_lds((const void*)(pa[j] + kt * BK),
+                                       (lds_void*)(stage + RPI * (w + NW * j) * BK), 16, 0, 0);
+  };
+  // weight block i of this lane: stage row w * (BN / NW) + 32 i + lane / 2, k half lane % 2
+  const int half = lane & 1;
+  const uint8_t* cp[NBL];
+  const uint8_t* sp[NBL];
+  int brow[NBL];
+#pragma unroll
+  for (int i = 0; i < NBL; ++i) {
+    brow[i] = w * (BN / NW) + 32 * i + (lane >> 1);
+    cp[i] = p.codes_row(e, n0 + brow[i]) + half * 16;
+    sp[i] = p.scales_row(e, n0 + brow[i]) + half;
+  }
+  struct Codes { u32x4 c[NBL]; uint32_t s[NBL]; };
+  auto load_codes = [&](Codes& C, int kt) {
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+      C.c[i] = *reinterpret_cast<const u32x4*>(cp[i] + kt * (BK / 2));
+      C.s[i] = sp[i][kt * (BK / 32)];
+    }
+  };
+  // decode this lane's blocks of stage kt and write them as bf16 into the stage's weight rows
+  auto store_b = [&](const Codes& C, int kt) {
+    uint16_t* stage = &smem[kt % NS][0];
+#pragma unroll
+    for (int i = 0; i < NBL; ++i) {
+      const int row = BM + brow[i];
+      const float sc = mx_scale(C.s[i]);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int ch = half * 4 + d;
+        *reinterpret_cast<bf16x8*>(stage + row * BK + ((ch ^ swz(row)) << 3)) = mx_decode8(C.c[i][d], sc);
+      }
+    }
+  };
+
+  const int wm = w / WGN, wn = w % WGN;
+  const int r16 = lane & 15, kq = lane >> 4;
+  f32x4 acc[TN][TM];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: codes 0 and 1 in flight, stage 0 (tokens by DMA, weights decoded)
+  Codes C0, C1;
+  issue_a(0);
+  load_codes(C0, 0);
+  if (nk > 1) load_codes(C1, 1);
+  store_b(C0, 0);
+  if (nk > 2) load_codes(C0, 2);
+
+  constexpr int KS = BK / 32;
+  auto iter = [&](int kt, Codes& Cn) {
+    // this stage's token rows (own DMA, issued before the last code loads) and
+    // weight rows (own LDS writes), then everyone's via the barrier
+    if (kt + 2 < nk || (kt == 0 && nk > 2)) wait_vmcnt<NCL>(); else wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's weight writes
+    stage_barrier();
+    const uint16_t* st = &smem[kt % NS][0];
+    bf16x8 xf[KS][TM], wf[KS][TN];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int q = ks * 4 + kq;
+#pragma unroll
+      for (int tt = 0; tt < TM; ++tt) {
+        const int row = wm * (BM / 2) + tt * 16 + r16;
+        if (wm * (BM / 2) + tt * 16 < mcount)
+          xf[ks][tt] = *reinterpret_cast<const bf16x8*>(st + row * BK + ((q ^ swz(row)) << 3));
+      }
+#pragma unroll
+      for (int gi = 0; gi < TN; ++gi) {
+        const int row = BM + wn * (BN / WGN) + gi * 16 + r16;
+        wf[ks][gi] = *reinterpret_cast<const bf16x8*>(st + row * BK + ((q ^ swz(row)) << 3));
+      }
+    }
+    if (kt + 1 < nk) {
+      issue_a(kt + 1);
+      store_b(Cn, kt + 1);                 // codes kt + 1, loaded two iterations ago
+      if (kt + 3 < nk) load_codes(Cn, kt + 3);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int tt = 0; tt < TM; ++tt)
+        if (wm * (BM / 2) + tt * 16 < mcount)
+#pragma unroll
+          for (int gi = 0; gi < TN; ++gi) acc[gi][tt] = mfma_bf16(wf[ks][gi], xf[ks][tt], acc[gi][tt]);
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    iter(kt, C1);
+    if (kt + 1 < nk) iter(kt + 1, C0);
+  }
+
+  const int ncol = (lane >> 4) * 4;
+#pragma unroll
+  for (int gi = 0; gi < TN; ++gi)
+#pragma unroll
+    for (int tt = 0; tt < TM; ++tt) {
+      const int i = wm * (BM / 2) + tt * 16 + r16;
+      if (i < mcount) p.store(e, m0 + i, n0 + wn * (BN / WGN) + gi * 16 + ncol, acc[gi][tt]);
+    }
+}
+
 // Tile shapes used per problem (token rows x weight rows), from a sweep on
 // the full-shape prefill problems.  Expert GEMMs use 128-row token tiles
 // (with ~352 rows per expert at the prefill batch a 256-row tile would pad
@@ -343,6 +494,26 @@ hipError_t tiled_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, in
 hipError_t tiled_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles, int max_tiles,
                           hipStream_t s) {
   return launch_expert(p, tiles, ntiles, max_tiles, s);
+}
+
+// MXFP4 weights: 128 x 256 tiles (128 x 512 needs more than the 256
+// registers two waves per SIMD allow, and spills).
+template <class P>
+static hipError_t launch_expert_mx(const P& p, const Tile* tiles, const int* ntiles,
+                                   int max_tiles, hipStream_t s) {
+  constexpr int BN = 256;
+  const long grid = xcd_grid((long)max_tiles * (p.N() / BN));
+  if (grid <= 0) return hipSuccess;
+  tiled_mx_kernel<P, kExpBM, BN, kWGN><<<grid, 128 * kWGN, 0, s>>>(p, tiles, ntiles);
+  return hipGetLastError();
+}
+hipError_t tiled_mx_exp_up(const ExpUpMx& p, const Tile* tiles, const int* ntiles, int max_tiles,
+                           hipStream_t s) {
+  return launch_expert_mx(p, tiles, ntiles, max_tiles, s);
+}
+hipError_t tiled_mx_exp_down(const ExpDownMx& p, const Tile* tiles, const int* ntiles,
+                             int max_tiles, hipStream_t s) {
+  return launch_expert_mx(p, tiles, ntiles, max_tiles, s);
 }
 
 }  // namespace lmoe

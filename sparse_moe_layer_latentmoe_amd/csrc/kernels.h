@@ -54,6 +54,12 @@ hipError_t stream_mx_exp_up(const ExpUpMx& p, const Tile* tiles, const int* ntil
                             int max_tiles, hipStream_t s);
 hipError_t stream_mx_exp_down(const ExpDownMx& p, const Tile* tiles, const int* ntiles,
                               int max_tiles, hipStream_t s);
+// The LDS-tiled expert GEMMs with MXFP4 weights (large batches; same
+// dimension requirements and tile list as tiled_exp_up / tiled_exp_down).
+hipError_t tiled_mx_exp_up(const ExpUpMx& p, const Tile* tiles, const int* ntiles, int max_tiles,
+                           hipStream_t s);
+hipError_t tiled_mx_exp_down(const ExpDownMx& p, const Tile* tiles, const int* ntiles,
+                             int max_tiles, hipStream_t s);
 
 // Router: fp32 logits, then per token sigmoid / bias / top-K / weights.  The
 // logits GEMM may split k over router_splits(T, E, R) partial [T, E] arrays

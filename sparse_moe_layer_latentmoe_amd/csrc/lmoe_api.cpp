@@ -349,9 +349,8 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
     dense = T <= kSplitMaxTokens ? Dense::kSplit : Dense::kTiled;
   const bool mxfp4 = c.expert_format == LMOE_EXPERTS_MXFP4;
   const bool expert_tiled =
-      !mxfp4 && tiled_ok &&
-      (c.path == LMOE_PATH_TILED ||
-       (c.path == LMOE_PATH_AUTO && static_cast<long>(T) * K > 32L * E));
+      tiled_ok && (c.path == LMOE_PATH_TILED ||
+                   (c.path == LMOE_PATH_AUTO && static_cast<long>(T) * K > 32L * E));
   const int tile_m = expert_tiled ? tiled_block_m() : kStreamTileM;
   const int ntile_max = static_cast<int>(max_tiles(c, T, tile_m));
 
@@ -446,7 +445,9 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   if (!mark()) return LMOE_ERR_HIP;
   if (mxfp4) {
     ExpUpMx pup{z16, rows_tok, h->w.expert_up_mxfp4, h->w.expert_up_scale, H, R, F};
-    if (!ok(stream_mx_exp_up(pup, tiles, ntiles, ntile_max, s))) return LMOE_ERR_HIP;
+    if (!ok(expert_tiled ? tiled_mx_exp_up(pup, tiles, ntiles, ntile_max, s)
+                         : stream_mx_exp_up(pup, tiles, ntiles, ntile_max, s)))
+      return LMOE_ERR_HIP;
   } else {
     ExpUp pup{z16, rows_tok, h->w.expert_up, H, R, F};
     if (!ok(expert_tiled ? tiled_exp_up(pup, tiles, ntiles, ntile_max, s)
@@ -456,7 +457,9 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   if (!mark()) return LMOE_ERR_HIP;
   if (mxfp4) {
     ExpDownMx pdn{H, h->w.expert_down_mxfp4, h->w.expert_down_scale, O, R, F};
-    if (!ok(stream_mx_exp_down(pdn, tiles, ntiles, ntile_max, s))) return LMOE_ERR_HIP;
+    if (!ok(expert_tiled ? tiled_mx_exp_down(pdn, tiles, ntiles, ntile_max, s)
+                         : stream_mx_exp_down(pdn, tiles, ntiles, ntile_max, s)))
+      return LMOE_ERR_HIP;
   } else {
     ExpDown pdn{H, h->w.expert_down, O, R, F};
     if (!ok(expert_tiled ? tiled_exp_down(pdn, tiles, ntiles, ntile_max, s)

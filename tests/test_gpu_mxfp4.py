@@ -89,16 +89,22 @@ def mx_weights(inp):
     return w
 
 
-@pytest.mark.parametrize("shape,tokens", [(MX_SMALL, 64), (MX_SMALL, 1), (MX_SMALL, 37),
-                                          (MX_WIDE, 1), (MX_WIDE, 37), (MX_WIDE, 64),
-                                          (MX_WIDE, 200), (MEDIUM, 129), (MEDIUM, 300)])
-def test_mxfp4_forward_matches_oracle(dev, shape, tokens):
+# (shape, tokens, path): AUTO streams the experts for few tokens per expert
+# and takes the LDS-tiled MXFP4 GEMMs for many (MEDIUM at T = 300: 1800 slots
+# over 32 experts); TILED forces them wherever the widths allow it.
+@pytest.mark.parametrize("shape,tokens,path", [
+    (MX_SMALL, 64, pkg.PATH_AUTO), (MX_SMALL, 1, pkg.PATH_AUTO), (MX_SMALL, 37, pkg.PATH_AUTO),
+    (MX_WIDE, 1, pkg.PATH_AUTO), (MX_WIDE, 37, pkg.PATH_AUTO), (MX_WIDE, 64, pkg.PATH_AUTO),
+    (MX_WIDE, 200, pkg.PATH_AUTO), (MEDIUM, 129, pkg.PATH_AUTO), (MEDIUM, 300, pkg.PATH_AUTO),
+    (MEDIUM, 1, pkg.PATH_TILED), (MEDIUM, 64, pkg.PATH_TILED), (MX_WIDE, 200, pkg.PATH_TILED),
+])
+def test_mxfp4_forward_matches_oracle(dev, shape, tokens, path):
     wl = li.Workload("mxfp4", shape, tokens)
     say(f"[mxfp4 forward E={shape.n_routed_experts} R={shape.moe_latent_size} "
-        f"F={shape.moe_intermediate_size} T={tokens}]")
+        f"F={shape.moe_intermediate_size} T={tokens} path={path}]")
     inp = li.make_inputs(wl, dev)
     w = mx_weights(inp)
-    layer = pkg.LatentMoE(shape, w, tokens, expert_format=pkg.EXPERTS_MXFP4)
+    layer = pkg.LatentMoE(shape, w, tokens, path=path, expert_format=pkg.EXPERTS_MXFP4)
     g = run_gpu(layer, inp.x)
     check_properties(g, shape, tokens)
     hw = mxfp4_host_weights(inp, eager_experts=True)
@@ -116,18 +122,20 @@ def test_mxfp4_forward_matches_oracle(dev, shape, tokens):
 
 
 @pytest.mark.fullshape
-def test_mxfp4_decode_full_shape(dev):
-    """The decode batch at full shape with MXFP4 experts: properties on every
+@pytest.mark.parametrize("name,rows", [("decode", [0, 13, 31]), ("prefill", [0, 4097, 8191])])
+def test_mxfp4_full_shape(dev, name, rows):
+    """The decode batch (weight streaming) and the prefill batch (LDS-tiled
+    MXFP4 GEMMs) at full shape with MXFP4 experts: properties on every
     token, the oracle on three sampled tokens (every expert they use
     quantised by the oracle and compared with the library's codes)."""
-    wl = li.workload("decode")
-    say("[mxfp4 full decode]")
+    wl = li.workload(name)
+    say(f"[mxfp4 full {name}]")
     inp = li.make_inputs(wl, dev)
     w = mx_weights(inp)
     layer = pkg.LatentMoE(wl.shape, w, wl.tokens, expert_format=pkg.EXPERTS_MXFP4)
     g = run_gpu(layer, inp.x)
     check_properties(g, wl.shape, wl.tokens)
-    rows = np.array([0, 13, wl.tokens - 1])
+    rows = np.array(rows)
     # the oracle quantises the touched experts itself, from the bf16 weights
     hw = mxfp4_host_weights(inp)
     used = np.unique(g.idx[rows])
