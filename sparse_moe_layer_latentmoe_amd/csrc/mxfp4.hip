@@ -187,27 +187,33 @@ __global__ __launch_bounds__(NW * 64) void stream_mx_kernel(P p, const Tile* til
   }
 }
 
-// Grouped expert GEMM for K a multiple of 512 (codes and scales 16-byte
-// aligned, N a multiple of WPG*RG*16).  Work-group = WPG waves on one 16-row
-// token tile, wave w on its own RG*16 weight rows over the whole k range (no
-// reduction).  k runs in 256-k stages: per stage a lane loads RG x 2 code
-// blocks (the two halves of each code line together) and reads its 4 x 2 token
-// fragments from LDS; the stage's token tile (16 rows x 256 k) is copied into
-// LDS by the whole work-group one stage ahead (double buffer, one barrier per
-// stage), and the scales come one 16-byte load per row for a pair of stages,
-// one pair ahead.  Work items (tile, row block) are taken XCD-major.
-template <class P, int RG, int WPG>
+// Grouped expert GEMM for K a multiple of 512 KS (codes and scales 16-byte
+// aligned, N a multiple of (WPG / KS) RG 16).  Work-group = WPG waves on one
+// 16-row token tile: WPG / KS row groups of RG * 16 weight rows, each split
+// over KS waves along k (KS = 1: one wave per row group over the whole k
+// range; KS > 1 shortens the work items, so that the last round of
+// work-groups on the chip is short, and adds the k parts in LDS in a fixed
+// order).  k runs in 256-k stages: per stage a lane loads RG x 2 code blocks
+// (the two halves of each code line together) and reads its 4 x 2 token
+// fragments from LDS; the stage's token tile (16 rows x 256 k for each k
+// part) is copied into LDS by the whole work-group one stage ahead (double
+// buffer, one barrier per stage), and the scales come one 16-byte load per
+// row for a pair of stages, one pair ahead.  Work items (tile, row block) are
+// taken XCD-major.
+template <class P, int RG, int WPG, int KS>
 __global__ __launch_bounds__(WPG * 64) void stream_mx_shared_kernel(P p, const Tile* tiles,
                                                                     const int* ntiles) {
   constexpr int XROW = 256 + 8;         // bf16 per LDS token row (16-byte pad: no bank conflicts)
-  constexpr int XP = 512 / (WPG * 64);  // 16-byte pieces of a stage's token tile per thread
-  static_assert(XP >= 1 && XP * WPG * 64 == 512, "WPG must divide 8");
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][16 * XROW];
+  constexpr int XT = 16 * XROW;         // one k part's token tile
+  constexpr int XP = KS * 512 / (WPG * 64);  // 16-byte token pieces per thread per stage
+  constexpr int NRG = WPG / KS;         // row groups per work-group
+  static_assert(XP >= 1 && XP * WPG * 64 == KS * 512 && NRG * KS == WPG, "WPG, KS");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][KS * XT];
 
   // Consecutive blocks go to the 8 XCDs in turn; block b runs work item
   // (b % 8) * (n / 8) + b / 8 so that the items of one tile (consecutive)
   // share an XCD and its L2.  Only the live tiles' items are numbered.
-  const int nwg = p.N() / (WPG * 16 * RG);
+  const int nwg = p.N() / (NRG * 16 * RG);
   const int nwork = *ntiles * nwg;
   const int b = blockIdx.x;
   if (b >= nwork) return;
@@ -219,28 +225,31 @@ __global__ __launch_bounds__(WPG * 64) void stream_mx_shared_kernel(P p, const T
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
-  const int nst = p.K() / 256;  // even
-  const int n0 = (nb * WPG + w) * (16 * RG);
+  const int rgw = w / KS, kh = w % KS;  // this wave's row group and k part
+  const int klen = p.K() / KS;
+  const int nst = klen / 256;           // stages per k part (even)
+  const int n0 = (nb * NRG + rgw) * (16 * RG);
 
   const uint8_t* cw[RG];
   const uint8_t* sw[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g) {
     const int row = n0 + g * 16 + r16;
-    cw[g] = p.codes_row(e, row) + q * 16;
-    sw[g] = p.scales_row(e, row);
+    cw[g] = p.codes_row(e, row) + kh * (klen / 2) + q * 16;
+    sw[g] = p.scales_row(e, row) + kh * (klen / 32);
   }
   // token rows past the tile's count copy the tile's first row (not stored)
   const uint16_t* xsrc[XP];
   int xdst[XP];
 #pragma unroll
   for (int j = 0; j < XP; ++j) {
-    const int piece = j * WPG * 64 + threadIdx.x;
+    const int gp = j * WPG * 64 + threadIdx.x;
+    const int part = gp / 512, piece = gp % 512;
     const int row = piece >> 5, col = (piece & 31) * 8;
-    xsrc[j] = p.a_row(m0 + (row < mcount ? row : 0)) + col;
-    xdst[j] = row * XROW + col;
+    xsrc[j] = p.a_row(m0 + (row < mcount ? row : 0)) + part * klen + col;
+    xdst[j] = part * XT + row * XROW + col;
   }
-  const int xrd = r16 * XROW + q * 32;
+  const int xrd = kh * XT + r16 * XROW + q * 32;
 
   f32x4 acc[RG];
 #pragma unroll
@@ -313,9 +322,26 @@ __global__ __launch_bounds__(WPG * 64) void stream_mx_shared_kernel(P p, const T
   }
 
   const int ncol = q * 4;
+  if constexpr (KS == 1) {
 #pragma unroll
-  for (int g = 0; g < RG; ++g)
-    if (r16 < mcount) p.store(e, m0 + r16, n0 + g * 16 + ncol, acc[g]);
+    for (int g = 0; g < RG; ++g)
+      if (r16 < mcount) p.store(e, m0 + r16, n0 + g * 16 + ncol, acc[g]);
+  } else {
+    // k parts added in part order (deterministic)
+    __shared__ f32x4 red[KS][NRG][RG][64];
+#pragma unroll
+    for (int g = 0; g < RG; ++g) red[kh][rgw][g][lane] = acc[g];
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        f32x4 sm = red[0][rgw][g][lane];
+#pragma unroll
+        for (int v = 1; v < KS; ++v) sm += red[v][rgw][g][lane];
+        if (r16 < mcount) p.store(e, m0 + r16, n0 + g * 16 + ncol, sm);
+      }
+    }
+  }
 }
 
 // The shared-token kernel where its conditions hold; otherwise the general
@@ -327,9 +353,18 @@ static hipError_t launch_mx(const P& p, const Tile* tiles, const int* ntiles, in
   constexpr int kSharedRG = 2, kSharedWPG = 8;
   const bool aligned = ((reinterpret_cast<uintptr_t>(p.codes) | reinterpret_cast<uintptr_t>(p.scales)) & 15) == 0;
   if (p.K() % 512 == 0 && p.N() % (kSharedWPG * 16 * kSharedRG) == 0 && aligned) {
+    // long k ranges (the down projection, k = 5120) in two parts: measured at
+    // the decode batch 0.403 vs 0.435 ms (the work-groups' last round on the
+    // chip is shorter); the up projection (k = 2048) is not faster that way
+    if (p.K() >= 4096 && p.K() % 1024 == 0) {
+      const long grid = (long)max_tiles * (p.N() / (kSharedWPG / 2 * 16 * kSharedRG));
+      if (grid <= 0) return hipSuccess;
+      stream_mx_shared_kernel<P, kSharedRG, kSharedWPG, 2><<<grid, kSharedWPG * 64, 0, s>>>(p, tiles, ntiles);
+      return hipGetLastError();
+    }
     const long grid = (long)max_tiles * (p.N() / (kSharedWPG * 16 * kSharedRG));
     if (grid <= 0) return hipSuccess;
-    stream_mx_shared_kernel<P, kSharedRG, kSharedWPG><<<grid, kSharedWPG * 64, 0, s>>>(p, tiles, ntiles);
+    stream_mx_shared_kernel<P, kSharedRG, kSharedWPG, 1><<<grid, kSharedWPG * 64, 0, s>>>(p, tiles, ntiles);
     return hipGetLastError();
   }
   constexpr int RG = 4;

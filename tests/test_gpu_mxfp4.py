@@ -22,6 +22,8 @@ MX_SMALL = li.LayerShape(256, 128, 16, 4, 256, 512, 5.0)
 # latent and expert widths multiples of 512: both expert GEMMs take the
 # shared-token kernel (MX_SMALL takes the general one, MEDIUM one of each)
 MX_WIDE = li.LayerShape(512, 512, 16, 4, 1024, 512, 5.0)
+# expert width 4096: the down projection's k range is split in two parts
+MX_LONG = li.LayerShape(512, 512, 16, 4, 4096, 512, 5.0)
 
 
 @pytest.fixture(scope="module")
@@ -97,6 +99,7 @@ def mx_weights(inp):
     (MX_WIDE, 1, pkg.PATH_AUTO), (MX_WIDE, 37, pkg.PATH_AUTO), (MX_WIDE, 64, pkg.PATH_AUTO),
     (MX_WIDE, 200, pkg.PATH_AUTO), (MEDIUM, 129, pkg.PATH_AUTO), (MEDIUM, 300, pkg.PATH_AUTO),
     (MEDIUM, 1, pkg.PATH_TILED), (MEDIUM, 64, pkg.PATH_TILED), (MX_WIDE, 200, pkg.PATH_TILED),
+    (MX_LONG, 1, pkg.PATH_AUTO), (MX_LONG, 37, pkg.PATH_AUTO),
 ])
 def test_mxfp4_forward_matches_oracle(dev, shape, tokens, path):
     wl = li.Workload("mxfp4", shape, tokens)
