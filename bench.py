@@ -150,6 +150,8 @@ def main():
                              "decode_mxfp4_block", "prefill_mxfp4"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one captured HIP graph of the forward")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -197,11 +199,25 @@ def main():
         layer.forward_into(inp.x, y)
     torch.cuda.synchronize()
 
+    graph = None
+    if args.graph:
+        # one forward captured into a HIP graph (the forward has no memset and
+        # no host synchronisation); its replays are the timed steps
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            layer.forward_into(inp.x, y)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+
     # Timed region: K forwards with nothing else on the stream.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        layer.forward_into(inp.x, y)
+        if graph is not None:
+            graph.replay()
+        else:
+            layer.forward_into(inp.x, y)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
@@ -284,6 +300,7 @@ def main():
         "layer_roofline": layer_roof,
         "us_per_layer": round(ms * 1e3, 2),
         "stages_ms": {k: round(v, 5) for k, v in stage_ms.items()},
+        "launch": "replays of one captured HIP graph" if graph is not None else "direct calls",
         "stage_timing": f"{nf} further forwards with per-stage HIP events "
                         f"({ms_events:.4f} ms/step with the events)",
     }
