@@ -1,0 +1,53 @@
+"""The benchmark's roofline accounting on the CPU: the algorithmic bytes and
+flops that every roofline fraction divides by, pinned to the page's layer
+totals ("Nemotron 3 Ultra 架构深度拆解报告", §2.3.4 / §3.1.3: 10.74 G expert
+parameters per MoE layer, 20.97 M per expert) and to counts done by hand for
+the benchmark batches."""
+
+import bench
+import lmoe_inputs as li
+
+
+def test_weights_read_once_add_up_to_the_layer():
+    sh = li.FULL
+    E = sh.n_routed_experts
+    b, _ = bench.stage_work(sh, 0, E)          # no tokens: weights only
+    # every expert touched: the page's 10.74 G expert parameters, 2 bytes each, per GEMM half
+    assert b["expert_up"] + b["expert_down"] == 2 * 10_737_418_240
+    assert b["expert_up"] == 2 * 20_971_520 // 2 * E
+    # fc1_latent + fc2_latent + shared up + shared down in bf16, the gate in fp32
+    D, R, S = sh.hidden_size, sh.moe_latent_size, sh.moe_shared_expert_intermediate_size
+    assert b["proj_latent"] + b["proj_out"] + b["shared_up"] == 2 * (2 * D * R + 2 * D * S)
+    assert b["router_logits"] == 4 * E * R
+
+
+def test_decode_batch_expert_bytes_by_hand():
+    # T = 32 tokens, 22 experts each: 704 slots; 375 distinct experts touched
+    b, f = bench.stage_work(li.FULL, 32, 375)
+    weights = 375 * 5120 * 2048 * 2
+    acts = 704 * 2048 * 2 + 704 * 5120 * 2       # gathered latent rows in, expert hidden out
+    assert b["expert_up"] == weights + acts == 7_874_412_544
+    assert f["expert_up"] == 2 * 704 * 2048 * 5120
+    # MXFP4: half a byte per weight plus one scale byte per 32
+    bm, _ = bench.stage_work(li.FULL, 32, 375, bench.MXFP4_BYTES)
+    assert bm["expert_up"] == 375 * 5120 * 2048 // 2 + 375 * 5120 * 2048 // 32 + acts
+
+
+def test_prefill_flops_per_token():
+    sh = li.FULL
+    _, f = bench.stage_work(sh, 8192, 512)
+    # the MFMA GEMMs (the fp32 gate and the combine's vector adds are not bf16 MFMA work)
+    gemms = ("proj_latent", "shared_up", "expert_up", "expert_down", "proj_out")
+    assert sum(f[k] for k in gemms) == bench.bf16_flops(sh, 8192)
+    # 2 (2 D R + 2 K R F + 2 D S) per token: the page's ~1.33 GFLOP less the gate
+    assert round(bench.bf16_flops(sh, 1) / 1e9, 4) == 1.3254
+
+
+def test_block_fusion_adds_its_activation_bytes():
+    sh = li.FULL
+    b0, _ = bench.stage_work(sh, 32, 375)
+    b1, _ = bench.stage_work(sh, 32, 375, block=True)
+    D = sh.hidden_size
+    # pre-norm: h and gamma read, bf16(gamma h) written, 1/rms written; residual: h read
+    assert b1["proj_latent"] - b0["proj_latent"] == 32 * D * 2 + D * 2 + 32 * D * 2 + 32 * 4
+    assert b1["proj_out"] - b0["proj_out"] == 32 * D * 2
