@@ -89,6 +89,16 @@ def test_block_with_mxfp4_experts(dev):
     run_block(dev, MX_WIDE, 37, BOTH, expert_format=pkg.EXPERTS_MXFP4)
 
 
+@pytest.mark.parametrize("tokens,path", [(37, pkg.PATH_AUTO), (200, pkg.PATH_TILED)])
+def test_every_option_at_once(dev, tokens, path):
+    """Group-limited routing (4 groups of 4, keep 2), MXFP4 experts and both
+    block steps in one layer, on the weight-streaming and the tiled path."""
+    from dataclasses import replace
+    shape = replace(MX_WIDE, n_group=4, topk_group=2)
+    g, _ = run_block(dev, shape, tokens, BOTH, path=path, expert_format=pkg.EXPERTS_MXFP4)
+    assert max(len(set((row // 4).tolist())) for row in g.idx) <= 2
+
+
 def test_block_output_is_residual_plus_layer(dev):
     """The residual alone changes nothing but the add: y(fuse=RESIDUAL) is
     the bf16 rounding of h + the unfused layer's fp32 result, so it stays
