@@ -138,6 +138,23 @@ def cpu_baseline(inp, sh, n_tokens):
                        f"{len(os.sched_getaffinity(0))})")}
 
 
+def near_ties(z32, wg, bias, sh, eps=1e-6):
+    """Tokens whose K-th and (K+1)-th selection scores (sigmoid(z Wg^T) + bias,
+    from the layer's own fp32 latent, evaluated in float64) differ by less
+    than eps: where rounding may decide which expert is chosen.  Reported
+    only for ungrouped routing (None otherwise); a diagnostic computed after
+    the first forward, outside the timed region."""
+    import torch
+    K = sh.num_experts_per_tok
+    if sh.n_group != 1 or K >= sh.n_routed_experts:
+        return None
+    sel = torch.sigmoid(z32.double() @ wg.double().t()) + bias.double()
+    top = torch.topk(sel, K + 1, dim=1).values
+    gap = top[:, K - 1] - top[:, K]
+    return {"count": int((gap < eps).sum().item()), "min_gap": float(gap.min().item()),
+            "eps": eps}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,8 +206,11 @@ def main():
                           fuse=pkg.FUSE_BLOCK if block else 0)
     y = torch.empty_like(inp.x)
     counts = torch.empty(sh.n_routed_experts, dtype=torch.int32, device=dev)
-    layer.forward_into(inp.x, y, pkg.Taps(expert_counts=counts))
+    z_tap = torch.empty(T, sh.moe_latent_size, dtype=torch.float32, device=dev)
+    layer.forward_into(inp.x, y, pkg.Taps(expert_counts=counts, z_f32=z_tap))
     torch.cuda.synchronize()
+    ties = near_ties(z_tap, inp.router, inp.router_bias, sh)
+    del z_tap
     U = int((counts > 0).sum().item())
     # load balance of the batch: busiest expert over the mean load, idle experts
     max_vio = float(counts.max().item()) / (T * sh.num_experts_per_tok / sh.n_routed_experts)
@@ -295,6 +315,7 @@ def main():
                                   if block else ""),
                    "tokens": T, "seed": wl.seed, "unique_experts": U,
                    "empty_experts": empty, "max_violation": round(max_vio, 3),
+                   "near_ties": ties,
                    "parallelism": "single GPU"},
         "roofline": roof,
         "layer_roofline": layer_roof,

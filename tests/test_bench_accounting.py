@@ -51,3 +51,25 @@ def test_block_fusion_adds_its_activation_bytes():
     # pre-norm: h and gamma read, bf16(gamma h) written, 1/rms written; residual: h read
     assert b1["proj_latent"] - b0["proj_latent"] == 32 * D * 2 + D * 2 + 32 * D * 2 + 32 * 4
     assert b1["proj_out"] - b0["proj_out"] == 32 * D * 2
+
+
+def test_near_ties_counts_boundary_ties_only():
+    """The benchmark's tie diagnostic on a hand-made router: four experts,
+    K = 2, one latent coordinate.  Logits 3, 2, 2, 1 put the 2nd and 3rd
+    scores level (a tie at the selection boundary); logits 3, 3, 1, 0 put
+    the tie inside the selected set (no tie at the boundary); a bias that
+    separates the two level experts by 1e-3 removes the tie."""
+    import torch
+    from dataclasses import replace
+    sh = replace(li.FULL, n_routed_experts=4, num_experts_per_tok=2, moe_latent_size=1)
+    z = torch.ones(1, 1)
+    zero = torch.zeros(4, dtype=torch.float64)
+    t = bench.near_ties(z, torch.tensor([[3.0], [2.0], [2.0], [1.0]]), zero, sh)
+    assert t["count"] == 1 and t["min_gap"] == 0.0
+    t = bench.near_ties(z, torch.tensor([[3.0], [3.0], [1.0], [0.0]]), zero, sh)
+    assert t["count"] == 0 and t["min_gap"] > 0.1
+    bias = torch.tensor([0.0, 1e-3, 0.0, 0.0], dtype=torch.float64)
+    t = bench.near_ties(z, torch.tensor([[3.0], [2.0], [2.0], [1.0]]), bias, sh)
+    assert t["count"] == 0 and abs(t["min_gap"] - 1e-3) < 1e-12
+    # group-limited routing: not reported
+    assert bench.near_ties(z, torch.ones(4, 1), zero, replace(sh, n_group=2, topk_group=1)) is None
