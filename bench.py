@@ -138,6 +138,54 @@ def cpu_baseline(inp, sh, n_tokens):
                        f"{len(os.sched_getaffinity(0))})")}
 
 
+def library_ceiling(inp, sh, T, stage_ms, reps=5):
+    """torch's bf16 matmul (the vendor GEMM library) on the layer's GEMM
+    shapes, timed like the layer's stages: a yardstick for the hand-written
+    GEMMs, never part of the layer.  Dense: the latent and shared-expert up
+    projections (x against W1, Wsu) and the output projection ([r | Hs]
+    against [W2 | Wsd]).  Experts: a batched stand-in with every expert
+    given the mean row count T K / E, contiguous rows (no gather, no fused
+    relu^2) and weights copied to [E, in, out]; the layer's own expert GEMMs
+    run on the real, uneven per-expert counts."""
+    import torch
+    import torch.nn.functional as Fn
+    D, R, S = sh.hidden_size, sh.moe_latent_size, sh.moe_shared_expert_intermediate_size
+    E, K, F = sh.n_routed_experts, sh.num_experts_per_tok, sh.moe_intermediate_size
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    res = {}
+    x = inp.x
+    res["proj_latent"] = (timed(lambda: Fn.linear(x, inp.fc1_latent)), 2.0 * T * D * R)
+    res["shared_up"] = (timed(lambda: Fn.linear(x, inp.shared_up)), 2.0 * T * D * S)
+    a_out = torch.randn(T, R + S, device=x.device, dtype=torch.bfloat16)
+    w_out = torch.cat([inp.fc2_latent, inp.shared_down], dim=1).contiguous()
+    res["proj_out"] = (timed(lambda: Fn.linear(a_out, w_out)), 2.0 * T * D * (R + S))
+    del a_out, w_out
+    M = max(1, round(T * K / E))
+    for name, w, kin, kout in (("expert_up", inp.expert_up, R, F),
+                               ("expert_down", inp.expert_down, F, R)):
+        wt = w.transpose(1, 2).contiguous()           # [E, in, out]
+        act = torch.randn(E, M, kin, device=x.device, dtype=torch.bfloat16)
+        res[name] = (timed(lambda: torch.bmm(act, wt)), 2.0 * E * M * kin * kout)
+        del wt, act
+    torch.cuda.empty_cache()
+    return {"what": "torch bf16 matmul on the same GEMM shapes (experts: batched stand-in, "
+                    f"{M} rows per expert)",
+            "library_ms": {k: round(v[0], 4) for k, v in res.items()},
+            "library_tflops": {k: round(v[1] / v[0] / 1e9, 1) for k, v in res.items()},
+            "layer_ms": {k: round(stage_ms[k], 4) for k in res if k in stage_ms}}
+
+
 def near_ties(z32, wg, bias, sh, eps=1e-6):
     """Tokens whose K-th and (K+1)-th selection scores (sigmoid(z Wg^T) + bias,
     from the layer's own fp32 latent, evaluated in float64) differ by less
@@ -167,6 +215,9 @@ def main():
                              "decode_mxfp4_block", "prefill_mxfp4"])
     ap.add_argument("--cpu-sample-tokens", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--library-ceiling", action="store_true",
+                    help="also time torch's bf16 matmul (the vendor GEMM library) on the "
+                         "layer's GEMM shapes, as a throughput yardstick (not the layer)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one captured HIP graph of the forward")
     args = ap.parse_args()
@@ -325,6 +376,8 @@ def main():
         "stage_timing": f"{nf} further forwards with per-stage HIP events "
                         f"({ms_events:.4f} ms/step with the events)",
     }
+    if args.library_ceiling:
+        out["library_ceiling"] = library_ceiling(inp, sh, T, stage_ms)
     if not args.no_cpu_baseline and not mxfp4 and not block:
         n = min(args.cpu_sample_tokens, T)
         out["cpu_baseline"] = cpu_baseline(inp, sh, n)
