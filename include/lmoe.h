@@ -150,7 +150,13 @@ size_t lmoe_workspace_size(const lmoe_config *cfg);
 
 /* Validate `cfg` and `w`, carve `workspace` (device memory of at least
  * lmoe_workspace_size(cfg) bytes, 256-byte aligned, caller-owned) and
- * return a host-side handle in *out.  No HIP call is made. */
+ * return a host-side handle in *out.  No HIP call is made.
+ * Debug aid: if the environment variable LMOE_DEBUG is set (and not "0")
+ * when the handle is created, lmoe_forward and lmoe_route synchronise the
+ * stream (and the handle's auxiliary stream) after every stage and return
+ * LMOE_ERR_HIP at the first stage whose launch or execution failed, naming
+ * it on stderr.  Same kernels and results; such calls block the host and
+ * cannot be captured into a HIP graph. */
 lmoe_status lmoe_create(const lmoe_config *cfg, const lmoe_weights *w, void *workspace,
                         size_t workspace_bytes, lmoe_handle **out);
 

@@ -23,6 +23,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -163,6 +165,8 @@ struct lmoe_handle {
   // profiling
   int prof_max = 0, prof_n = 0;
   std::vector<hipEvent_t> events;
+  // LMOE_DEBUG set (and not "0") at creation: synchronise after every stage
+  bool debug = false;
 
   template <class T>
   T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
@@ -208,6 +212,8 @@ lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, void* wor
   h->w = *w;
   h->ws = static_cast<char*>(workspace);
   h->L = L;
+  const char* dbg = std::getenv("LMOE_DEBUG");
+  h->debug = dbg && *dbg && std::strcmp(dbg, "0") != 0;
   *out = h;
   return LMOE_OK;
 }
@@ -313,6 +319,14 @@ lmoe_status lmoe_route(lmoe_handle* h, const float* z_f32, int32_t T, int32_t* t
                     c.num_experts_per_tok, c.n_group, c.topk_group, c.routed_scaling_factor,
                     topk_idx, topk_w, s) != hipSuccess)
     return LMOE_ERR_HIP;
+  if (h->debug) {
+    hipError_t e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) {
+      std::fprintf(stderr, "lmoe: route failed: %s\n", hipGetErrorString(e));
+      return LMOE_ERR_HIP;
+    }
+  }
   return LMOE_OK;
 }
 
@@ -408,6 +422,17 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
     return hipEventRecord(ev[stage++], s) == hipSuccess;
   };
   auto ok = [](hipError_t e) { return e == hipSuccess; };
+  // Debug mode: wait for the stage just launched (and the auxiliary stream)
+  // and report the first failure with the stage's name.
+  auto done = [&](const char* stage_name) -> bool {
+    if (!h->debug) return true;
+    hipError_t e = hipStreamSynchronize(s);
+    if (e == hipSuccess && h->aux) e = hipStreamSynchronize(h->aux);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e == hipSuccess) return true;
+    std::fprintf(stderr, "lmoe: stage %s failed: %s\n", stage_name, hipGetErrorString(e));
+    return false;
+  };
 
   // Shared expert's up projection on the auxiliary stream, forked from `s`
   // at the current point and joined before proj_out.
@@ -428,19 +453,23 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   if (!mark()) return LMOE_ERR_HIP;
   if (prenorm_fused && !ok(prenorm(x, h->w.norm_weight, T, D, c.norm_eps, xt, rn, s)))
     return LMOE_ERR_HIP;
-  if (fork_first && !fork_shared()) return LMOE_ERR_HIP;
+  if (prenorm_fused && !done("prenorm")) return LMOE_ERR_HIP;
+  if (fork_first && !(fork_shared() && done("shared_up"))) return LMOE_ERR_HIP;
   ProjIn platent{xin, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, 0, R, rscale};
-  if (!ok(proj_in(platent, s))) return LMOE_ERR_HIP;
-  if (!fork_first && !fork_shared()) return LMOE_ERR_HIP;
+  if (!ok(proj_in(platent, s)) || !done("proj_latent")) return LMOE_ERR_HIP;
+  if (!fork_first && !(fork_shared() && done("shared_up"))) return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
-  if (!ok(router_logits(z32, h->w.router, logits, T, E, R, s))) return LMOE_ERR_HIP;
+  if (!ok(router_logits(z32, h->w.router, logits, T, E, R, s)) || !done("router_logits"))
+    return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
   if (!ok(router_select(logits, h->w.router_bias, T, E, R, K, c.n_group, c.topk_group,
-                        c.routed_scaling_factor, idx, tw, s)))
+                        c.routed_scaling_factor, idx, tw, s)) ||
+      !done("router_select"))
     return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
   if (!ok(dispatch(idx, T, K, E, blockcnt, counts, offsets, rows_tok, inv, tiles, ntiles, tile_m,
-                   s)))
+                   s)) ||
+      !done("dispatch"))
     return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
   if (mxfp4) {
@@ -454,7 +483,7 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
                          : stream_exp_up(pup, tiles, ntiles, ntile_max, s)))
       return LMOE_ERR_HIP;
   }
-  if (!mark()) return LMOE_ERR_HIP;
+  if (!done("expert_up") || !mark()) return LMOE_ERR_HIP;
   if (mxfp4) {
     ExpDownMx pdn{H, h->w.expert_down_mxfp4, h->w.expert_down_scale, O, R, F};
     if (!ok(expert_tiled ? tiled_mx_exp_down(pdn, tiles, ntiles, ntile_max, s)
@@ -466,14 +495,15 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
                          : stream_exp_down(pdn, tiles, ntiles, ntile_max, s)))
       return LMOE_ERR_HIP;
   }
-  if (!mark()) return LMOE_ERR_HIP;
-  if (!ok(combine(O, inv, tw, T, K, R, r16, taps ? taps->r_latent : nullptr, s)))
+  if (!done("expert_down") || !mark()) return LMOE_ERR_HIP;
+  if (!ok(combine(O, inv, tw, T, K, R, r16, taps ? taps->r_latent : nullptr, s)) ||
+      !done("combine"))
     return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
   // join, then y = r W2^T + Hs Wsd^T (+ h with the block residual fused)
   if (!ok(hipStreamWaitEvent(s, h->join, 0))) return LMOE_ERR_HIP;
   ProjOut pout{r16, hs, h->w.fc2_latent, h->w.shared_down, y, T, D, R, S, resid};
-  if (!ok(proj_out(pout, s))) return LMOE_ERR_HIP;
+  if (!ok(proj_out(pout, s)) || !done("proj_out")) return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
 
   if (taps) {

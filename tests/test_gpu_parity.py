@@ -230,6 +230,33 @@ def test_deterministic_and_token_order_equivariant(dev):
         assert np.array_equal(c.idx, a.idx[perm.numpy()])
 
 
+@pytest.mark.parametrize("fuse", [0, pkg.FUSE_BLOCK])
+def test_debug_mode_gives_the_same_results(dev, monkeypatch, fuse):
+    """LMOE_DEBUG set when the handle is created: every stage is waited for
+    and checked; the forward (both tilings, with and without the block's
+    pre-norm stage) and the router entry point give the same results bit for
+    bit as a handle created without it."""
+    wl = medium(300)
+    inp = li.make_inputs(wl, dev)
+    w = weight_dict(inp)
+    if fuse:
+        w["norm_weight"] = li.make_norm_weight(wl, dev)
+    for path in (pkg.PATH_STREAM, pkg.PATH_TILED):
+        say(f"[debug mode path={path} fuse={fuse}]")
+        plain = pkg.LatentMoE(wl.shape, w, 300, path, fuse=fuse)
+        monkeypatch.setenv("LMOE_DEBUG", "1")
+        dbg = pkg.LatentMoE(wl.shape, w, 300, path, fuse=fuse)
+        monkeypatch.delenv("LMOE_DEBUG")
+        a, b = run_gpu(plain, inp.x), run_gpu(dbg, inp.x)
+        assert torch.equal(a.y, b.y) and np.array_equal(a.idx, b.idx)
+        assert np.array_equal(a.w, b.w) and np.array_equal(a.z32, b.z32)
+        z = torch.from_numpy(a.z32).to(dev)
+        ia, wa = plain.route(z)
+        ib, wb = dbg.route(z)
+        torch.cuda.synchronize()
+        assert torch.equal(ia, ib) and torch.equal(wa, wb)
+
+
 def test_smaller_batch_after_larger_on_one_handle(dev):
     # the workspace keeps the larger batch's contents; the smaller batch
     # (which may pick another tiling) must still match the oracle
