@@ -350,6 +350,9 @@ __global__ __launch_bounds__(128 * WGN) void tiled_mx_kernel(P p, const Tile* ti
     if (kt + 2 < nk || (kt == 0 && nk > 2)) wait_vmcnt<NCL>(); else wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's weight writes
     stage_barrier();
+    // the next stage's token DMA first (its buffer's last reads were the
+    // previous stage's): 2-4% faster than issuing it after the reads
+    if (kt + 1 < nk) issue_a(kt + 1);
     const uint16_t* st = &smem[kt % NS][0];
     bf16x8 xf[KS][TM], wf[KS][TN];
 #pragma unroll
@@ -368,7 +371,6 @@ __global__ __launch_bounds__(128 * WGN) void tiled_mx_kernel(P p, const Tile* ti
       }
     }
     if (kt + 1 < nk) {
-      issue_a(kt + 1);
       store_b(Cn, kt + 1);                 // codes kt + 1, loaded two iterations ago
       if (kt + 3 < nk) load_codes(Cn, kt + 3);
     }
