@@ -73,3 +73,18 @@ def test_near_ties_counts_boundary_ties_only():
     assert t["count"] == 0 and abs(t["min_gap"] - 1e-3) < 1e-12
     # group-limited routing: not reported
     assert bench.near_ties(z, torch.ones(4, 1), zero, replace(sh, n_group=2, topk_group=1)) is None
+
+
+def test_more_than_one_gpu_is_refused():
+    """The benchmark runs on one GPU: --gpus above 1 exits with status 2 and
+    a one-line JSON message, before touching torch or the library."""
+    import json
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60, cwd=root)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
