@@ -72,15 +72,24 @@ def stage_work(sh, T, U, expert_weight_bytes=2.0, block=False):
     return b, f
 
 
-def source_sha256():
-    """Hash of the device code the decode path runs (the kernel sources and
-    the device headers; not the LDS-tiled GEMM, which only runs for large
-    batches, nor the host-side launch code), to tell whether stored counter
-    data still describes the kernels being run."""
+# Device code each stored counter measurement depends on: the kernel sources
+# and device headers the workload runs (decode: weight streaming only; MTP
+# verify also takes the LDS-tiled split-k GEMMs for its dense projections).
+DECODE_SOURCES = ("gemm_stream.hip", "router.hip", "dispatch.hip", "gemm_problems.h",
+                  "lmoe_device.h")
+TRAFFIC_PROFILES = {
+    "decode": ("traffic_decode_T32.json", DECODE_SOURCES),
+    "mtp_verify": ("traffic_mtp_verify_T192.json", DECODE_SOURCES + ("gemm_tiled.hip",)),
+}
+
+
+def source_sha256(device=DECODE_SOURCES):
+    """Hash of the device code a workload runs (the kernel sources and the
+    device headers, not the host-side launch code), to tell whether stored
+    counter data still describes the kernels being run."""
     import glob
     import hashlib
     h = hashlib.sha256()
-    device = ("gemm_stream.hip", "router.hip", "dispatch.hip", "gemm_problems.h", "lmoe_device.h")
     for f in sorted(glob.glob(os.path.join(ROOT, "sparse_moe_layer_latentmoe_amd", "csrc", "*"))):
         if os.path.basename(f) not in device:
             continue
@@ -95,13 +104,16 @@ def measured_traffic(workload, stage):
     from the rocprofv3 counter runs kept under profiles/), or None when no
     such measurement exists for this workload or the kernels have changed
     since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_T32.json")
-    if workload != "decode" or not os.path.exists(path):
+    if workload not in TRAFFIC_PROFILES:
+        return None
+    fname, sources = TRAFFIC_PROFILES[workload]
+    path = os.path.join(ROOT, "profiles", fname)
+    if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
     st = d.get("stages", {}).get(stage)
-    if st is None or d.get("source_sha256") != source_sha256():
+    if st is None or d.get("source_sha256") != source_sha256(sources):
         return None
     return int(st["fetch_bytes"] + st["write_bytes"])
 
