@@ -88,3 +88,23 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
+
+
+def test_stored_traffic_profiles_use_the_benchmark_accounting():
+    """Each committed HBM-traffic profile records, per stage, the algorithmic
+    bytes that the benchmark's own accounting gives for the experts the
+    profiled batch touched, and its source list is the one the benchmark
+    checks its hash against."""
+    import json
+    import os
+    for workload, (fname, sources) in bench.TRAFFIC_PROFILES.items():
+        path = os.path.join(bench.ROOT, "profiles", fname)
+        d = json.load(open(path))
+        wl = li.workload(workload)
+        sb, _ = bench.stage_work(wl.shape, wl.tokens, d["unique_experts"])
+        assert set(d["stages"]) == set(sb)
+        for st, rec in d["stages"].items():
+            assert rec["algorithmic_bytes"] == int(sb[st]), (workload, st)
+            assert rec["fetch_bytes"] > 0
+        if "sources" in d:
+            assert tuple(d["sources"]) == tuple(sources)
