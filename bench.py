@@ -32,6 +32,10 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 HBM_BOUND = {"tiny", "decode", "mtp_verify", "decode_grouped", "decode_mxfp4",
              "mtp_verify_mxfp4"}
 MXFP4_BYTES = 0.5 + 1.0 / 32
+# Batches of at most this many tokens stream the dense weights, and run the
+# shared expert's down projection on the auxiliary stream (timed with
+# shared_up); the output projection then covers fc2_latent only.
+STREAM_DENSE_MAX_TOKENS = 64
 
 
 def stage_work(sh, T, U, expert_weight_bytes=2.0, block=False):
@@ -41,7 +45,10 @@ def stage_work(sh, T, U, expert_weight_bytes=2.0, block=False):
     0.5 + 1/32 for MXFP4: half a byte per element plus a scale byte per 32).
     ``block``: the block's pre-norm (timed inside proj_latent: h and gamma
     read, bf16(gamma h) and 1/rms written) and residual (h read by proj_out)
-    are fused in."""
+    are fused in.  For weight-streaming batches (T <= STREAM_DENSE_MAX_TOKENS)
+    the shared expert's down projection (Wsd and Hs read) is counted in the
+    stage it runs in, shared_up; the fp32 hand-over between the two launches
+    is not algorithmic traffic and is not counted."""
     D, R, E = sh.hidden_size, sh.moe_latent_size, sh.n_routed_experts
     K, F, S = sh.num_experts_per_tok, sh.moe_intermediate_size, sh.moe_shared_expert_intermediate_size
     slots = T * K
@@ -59,6 +66,11 @@ def stage_work(sh, T, U, expert_weight_bytes=2.0, block=False):
     if block:
         b["proj_latent"] += T * D * 2 + D * 2 + T * D * 2 + T * 4
         b["proj_out"] += T * D * 2
+    split = T <= STREAM_DENSE_MAX_TOKENS
+    if split:
+        moved = D * S * 2 + T * S * 2
+        b["shared_up"] += moved
+        b["proj_out"] -= moved
     f = {
         "proj_latent": 2 * T * D * R,
         "shared_up": 2 * T * D * S,
@@ -69,6 +81,9 @@ def stage_work(sh, T, U, expert_weight_bytes=2.0, block=False):
         "combine": 2 * slots * R,
         "proj_out": 2 * T * D * (R + S),
     }
+    if split:
+        f["shared_up"] += 2 * T * D * S
+        f["proj_out"] -= 2 * T * D * S
     return b, f
 
 

@@ -199,7 +199,10 @@ const char *lmoe_status_string(lmoe_status s);
  * 0..7 run back to back on the forward's stream (the last one, proj_out,
  * includes the wait for the auxiliary stream; the first, proj_latent,
  * includes the pre-norm kernel when it is fused); stage 8 ("shared_up") is
- * timed on the auxiliary stream and overlaps the stages before proj_out. */
+ * timed on the auxiliary stream and overlaps the stages before proj_out.
+ * For T <= 64 (weight-streaming projections) stage 8 also runs the shared
+ * expert's down projection and proj_out covers fc2_latent only, adding the
+ * shared output before its single rounding. */
 int32_t lmoe_num_stages(void);
 const char *lmoe_stage_name(int32_t i);
 

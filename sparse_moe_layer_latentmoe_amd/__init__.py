@@ -87,6 +87,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(
             f"{path} is missing: build the HIP library first "
             "(python -m sparse_moe_layer_latentmoe_amd._build)")
+    # torch ships its own HIP runtime under the same soname as the system's;
+    # whichever is loaded first serves the whole process.  Importing torch
+    # first keeps torch on the runtime it was built with (loading this
+    # library first made torch's allocations unusable for its launches).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     lib.lmoe_workspace_size.argtypes = [ctypes.POINTER(LmoeConfig)]

@@ -66,6 +66,9 @@ struct ProjIn {
 // over the concatenated k range gives their sum with a single rounding).
 // With the block's residual fused, resid (the block input h, bf16 [T, D]) is
 // added to the fp32 sums before that rounding.
+// The same sum in two launches (part 1 then part 2, weight-streaming path):
+// part 1 computes only Hs Wsd^T into ys (fp32 [T, D]); part 2 only r W2^T,
+// adds ys (and resid) to its fp32 sums and rounds once.  part 0: both at once.
 struct ProjOut {
   const uint16_t* r16;
   const uint16_t* hs;
@@ -74,21 +77,32 @@ struct ProjOut {
   uint16_t* y;
   int T, D, R, S;
   const uint16_t* resid;  // [T, D] or null
+  int part = 0;
+  float* ys = nullptr;    // [T, D] fp32 for parts 1 and 2
   static constexpr bool kGatherA = false;
-  __device__ const uint16_t* a_base0() const { return r16; }
+  __device__ const uint16_t* a_base0() const { return part == 1 ? hs : r16; }
   __device__ const uint16_t* a_base1() const { return hs; }
-  __device__ long lda0() const { return R; }
+  __device__ long lda0() const { return part == 1 ? S : R; }
   __device__ long lda1() const { return S; }
-  __device__ long ldb0() const { return R; }
+  __device__ long ldb0() const { return part == 1 ? S : R; }
   __device__ long ldb1() const { return S; }
   __host__ __device__ int N() const { return D; }
-  __host__ __device__ int K() const { return R + S; }
-  __host__ __device__ int K0() const { return R; }
-  __device__ const uint16_t* b_row0(int, int n) const { return w2 + (size_t)n * R; }
+  __host__ __device__ int K() const { return part == 0 ? R + S : (part == 1 ? S : R); }
+  __host__ __device__ int K0() const { return part == 0 ? R : K(); }
+  __device__ const uint16_t* b_row0(int, int n) const {
+    return part == 1 ? wsd + (size_t)n * S : w2 + (size_t)n * R;
+  }
   __device__ const uint16_t* b_row1(int, int n) const { return wsd + (size_t)n * S; }
-  __device__ const uint16_t* a_row0(int m) const { return r16 + (size_t)m * R; }
+  __device__ const uint16_t* a_row0(int m) const {
+    return part == 1 ? hs + (size_t)m * S : r16 + (size_t)m * R;
+  }
   __device__ const uint16_t* a_row1(int m) const { return hs + (size_t)m * S; }
   __device__ void store(int, int m, int n, f32x4 v) const {
+    if (part == 1) {
+      *reinterpret_cast<f32x4*>(ys + (size_t)m * D + n) = v;
+      return;
+    }
+    if (part == 2) v += *reinterpret_cast<const f32x4*>(ys + (size_t)m * D + n);
     if (resid) {
       const u16x4 h = *reinterpret_cast<const u16x4*>(resid + (size_t)m * D + n);
       v[0] += bf16_to_f32(h[0]);

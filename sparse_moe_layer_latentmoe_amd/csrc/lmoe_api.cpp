@@ -15,7 +15,9 @@
 // and, forked onto the handle's auxiliary stream (before proj_latent for
 // weight-streaming batches, after it otherwise) and joined before proj_out
 // (the shared expert only needs x):
-//   shared_up      x -> relu(x Wsu^T)^2                        (Step 7)
+//   shared_up      x -> Hs = relu(x Wsu^T)^2                   (Step 7)
+//                  [weight-streaming batches: then ys = Hs Wsd^T in fp32,
+//                   and proj_out computes r W2^T + ys]
 // The latent projection and the router/dispatch chain are latency-bound and
 // leave HBM idle; the shared expert's weight stream fills that time.
 #include <hip/hip_runtime.h>
@@ -104,8 +106,8 @@ long max_tiles(const lmoe_config& c, long T, int tile_m) {
 }
 
 struct Layout {
-  size_t xt, rn, z32, z16, hs, part, logits, idx, tw, counts, offsets, blockcnt, rows_tok, inv,
-      tiles, ntiles, h, o, r16, total;
+  size_t xt, rn, z32, z16, hs, ys, part, logits, idx, tw, counts, offsets, blockcnt, rows_tok,
+      inv, tiles, ntiles, h, o, r16, total;
 };
 
 Layout make_layout(const lmoe_config& c) {
@@ -126,6 +128,9 @@ Layout make_layout(const lmoe_config& c) {
   L.z32 = take(T * R * 4);
   L.z16 = take(T * R * 2);
   L.hs = take(T * S * 2);
+  // fp32 shared-expert output of weight-streaming batches (at most
+  // kStreamDenseMaxTokens tokens), computed on the auxiliary stream
+  L.ys = take(std::min<size_t>(T, kStreamDenseMaxTokens) * c.hidden_size * 4);
   // split-k partial sums of the dense GEMMs (any batch of at most
   // kSplitMaxTokens tokens may take the split path when the tiled GEMMs apply)
   const size_t D = c.hidden_size;
@@ -434,6 +439,12 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
     return false;
   };
 
+  // Weight-streaming batches: the shared expert's down projection also runs
+  // on the auxiliary stream (its weight stream fills HBM time the router and
+  // dispatch leave idle), into fp32 ys; proj_out then streams only W2 and
+  // adds ys before its single rounding.
+  const bool split_out = dense == Dense::kStream && T <= kStreamDenseMaxTokens;
+  float* ys = h->at<float>(h->L.ys);
   // Shared expert's up projection on the auxiliary stream, forked from `s`
   // at the current point and joined before proj_out.
   auto fork_shared = [&]() -> bool {
@@ -442,6 +453,10 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
     if (ev && !ok(hipEventRecord(ev[kMainStages + 1], h->aux))) return false;
     ProjIn pshared{xin, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, R, S, rscale};
     if (!ok(proj_in(pshared, h->aux))) return false;
+    if (split_out) {
+      ProjOut pdown{r16, hs, h->w.fc2_latent, h->w.shared_down, y, T, D, R, S, nullptr, 1, ys};
+      if (!ok(stream_proj_out(pdown, h->aux))) return false;
+    }
     if (ev && !ok(hipEventRecord(ev[kMainStages + 2], h->aux))) return false;
     return ok(hipEventRecord(h->join, h->aux));
   };
@@ -502,7 +517,8 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   if (!mark()) return LMOE_ERR_HIP;
   // join, then y = r W2^T + Hs Wsd^T (+ h with the block residual fused)
   if (!ok(hipStreamWaitEvent(s, h->join, 0))) return LMOE_ERR_HIP;
-  ProjOut pout{r16, hs, h->w.fc2_latent, h->w.shared_down, y, T, D, R, S, resid};
+  ProjOut pout{r16, hs, h->w.fc2_latent, h->w.shared_down, y, T, D, R, S, resid,
+               split_out ? 2 : 0, ys};
   if (!ok(proj_out(pout, s)) || !done("proj_out")) return LMOE_ERR_HIP;
   if (!mark()) return LMOE_ERR_HIP;
 

@@ -108,3 +108,22 @@ def test_stored_traffic_profiles_use_the_benchmark_accounting():
             assert rec["fetch_bytes"] > 0
         if "sources" in d:
             assert tuple(d["sources"]) == tuple(sources)
+
+
+def test_streaming_batches_count_the_shared_down_projection_where_it_runs():
+    """At T <= 64 the shared expert's down projection runs on the auxiliary
+    stream with its up projection: its weight bytes and flops move from
+    proj_out to shared_up, and the layer's totals do not change."""
+    import re
+    sh = li.FULL
+    D, R, S = sh.hidden_size, sh.moe_latent_size, sh.moe_shared_expert_intermediate_size
+    b, f = bench.stage_work(sh, 32, 375)
+    assert b["proj_out"] == D * R * 2 + 32 * R * 2 + 32 * D * 2
+    assert b["shared_up"] == S * D * 2 + 32 * D * 2 + 32 * S * 2 + D * S * 2 + 32 * S * 2
+    assert f["proj_out"] == 2 * 32 * D * R and f["shared_up"] == 4 * 32 * D * S
+    b65, f65 = bench.stage_work(sh, 65, 375)
+    assert b65["proj_out"] == D * (R + S) * 2 + 65 * (R + S) * 2 + 65 * D * 2
+    assert f["proj_out"] + f["shared_up"] == 2 * 32 * D * (R + S) + 2 * 32 * D * S
+    # the threshold is the library's own
+    src = open(bench.ROOT + "/sparse_moe_layer_latentmoe_amd/csrc/kernels.h").read()
+    assert int(re.search(r"kStreamDenseMaxTokens = (\d+)", src).group(1)) == bench.STREAM_DENSE_MAX_TOKENS
