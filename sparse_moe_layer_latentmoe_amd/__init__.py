@@ -190,6 +190,62 @@ def quantize_mxfp4(w, stream=None):
     return codes, scales
 
 
+def _expect(t, shape, dtype, what: str, contiguous: bool = True, device=None,
+            on_gpu: bool = True) -> None:
+    """Raise unless ``t`` is a GPU tensor of this dtype and shape (and
+    contiguous, and on ``device``, when asked): the C ABI takes bare
+    pointers, so a tensor of the wrong size or type would be read or written
+    out of bounds on the device."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if on_gpu and t.device.type != "cuda":
+        raise ValueError(f"{what}: must be a GPU tensor, got one on {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what}: on {t.device}, the layer is on {device}")
+
+
+def weight_specs(shape, expert_format: int = EXPERTS_BF16, fuse: int = 0) -> dict:
+    """{lmoe_weights field: (shape, torch dtype)} of the weights a layer with
+    this shape, expert format and fusion needs (the layouts of lmoe.h)."""
+    import torch
+    D, R, E = shape.hidden_size, shape.moe_latent_size, shape.n_routed_experts
+    F, S = shape.moe_intermediate_size, shape.moe_shared_expert_intermediate_size
+    bf16, f32, u8 = torch.bfloat16, torch.float32, torch.uint8
+    spec = {"fc1_latent": ((R, D), bf16), "router": ((E, R), f32), "router_bias": ((E,), f32),
+            "fc2_latent": ((D, R), bf16), "shared_up": ((S, D), bf16),
+            "shared_down": ((D, S), bf16)}
+    if expert_format == EXPERTS_MXFP4:
+        spec.update(expert_up_mxfp4=((E, F, R // 2), u8), expert_up_scale=((E, F, R // 32), u8),
+                    expert_down_mxfp4=((E, R, F // 2), u8),
+                    expert_down_scale=((E, R, F // 32), u8))
+    else:
+        spec.update(expert_up=((E, F, R), bf16), expert_down=((E, R, F), bf16))
+    if fuse & FUSE_PRENORM:
+        spec["norm_weight"] = ((D,), bf16)
+    return spec
+
+
+def check_weights(shape, weights: dict, expert_format: int = EXPERTS_BF16, fuse: int = 0,
+                  device=None) -> None:
+    """Raise unless ``weights`` holds every tensor the layer needs with the
+    right shape and dtype, on one GPU (non-contiguous ones are copied by the
+    layer)."""
+    spec = weight_specs(shape, expert_format, fuse)
+    for name, (shp, dt) in spec.items():        # presence, dtype and shape first
+        if weights.get(name) is None:
+            raise ValueError(f"weights[{name!r}] is required")
+        _expect(weights[name], shp, dt, f"weights[{name!r}]", contiguous=False, on_gpu=False)
+    for name, (shp, dt) in spec.items():        # then where they live
+        _expect(weights[name], shp, dt, f"weights[{name!r}]", contiguous=False, device=device)
+
+
 class LatentMoE:
     """One LatentMoE layer bound to caller-owned device weights.
 
@@ -210,7 +266,15 @@ class LatentMoE:
         ws_bytes = workspace_size(self.cfg)
         if ws_bytes == 0:
             raise LmoeError(LMOE_ERR_UNSUPPORTED, "lmoe_workspace_size")
-        dev = device if device is not None else weights["fc1_latent"].device
+        if device is None:
+            check_weights(shape, weights, expert_format, fuse)
+            dev = weights["fc1_latent"].device
+        else:
+            dev = torch.device(device)
+            if dev.index is None:
+                dev = torch.device(dev.type, torch.cuda.current_device())
+        check_weights(shape, weights, expert_format, fuse, dev)
+        self.device = dev
         self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         self.weights = {k: v.contiguous() for k, v in weights.items() if v is not None}
         self.wstruct = LmoeWeights(*[_ptr(self.weights.get(n)) for n, _ in LmoeWeights._fields_])
@@ -234,6 +298,21 @@ class LatentMoE:
 
     def forward_into(self, x, y, taps: Taps | None = None, stream=None) -> None:
         """y <- LatentMoE(x); x, y bf16 [T, D] device tensors."""
+        import torch
+        sh = self.shape
+        T = int(x.shape[0]) if getattr(x, "dim", lambda: 0)() == 2 else -1
+        D, R, K = sh.hidden_size, sh.moe_latent_size, sh.num_experts_per_tok
+        _expect(x, (T, D), torch.bfloat16, "x", device=self.device)
+        _expect(y, (T, D), torch.bfloat16, "y", device=self.device)
+        if taps is not None:
+            for name, shp, dt in (("z_f32", (T, R), torch.float32),
+                                  ("topk_idx", (T, K), torch.int32),
+                                  ("topk_w", (T, K), torch.float32),
+                                  ("expert_counts", (sh.n_routed_experts,), torch.int32),
+                                  ("r_latent", (T, R), torch.float32)):
+                t = getattr(taps, name)
+                if t is not None:
+                    _expect(t, shp, dt, f"taps.{name}", device=self.device)
         ts = taps.as_struct() if taps is not None else None
         st = self.lib.lmoe_forward(self.handle, _ptr(x), int(x.shape[0]), _ptr(y),
                                    _stream_handle(stream),
@@ -252,8 +331,10 @@ class LatentMoE:
     def route(self, z_f32, stream=None):
         """(topk_idx int32 [T, K], topk_w fp32 [T, K]) from a given fp32 latent."""
         import torch
-        T = int(z_f32.shape[0])
+        T = int(z_f32.shape[0]) if getattr(z_f32, "dim", lambda: 0)() == 2 else -1
         K = self.shape.num_experts_per_tok
+        _expect(z_f32, (T, self.shape.moe_latent_size), torch.float32, "z_f32",
+                device=self.device)
         idx = torch.empty((T, K), dtype=torch.int32, device=z_f32.device)
         w = torch.empty((T, K), dtype=torch.float32, device=z_f32.device)
         st = self.lib.lmoe_route(self.handle, _ptr(z_f32), T, _ptr(idx), _ptr(w),

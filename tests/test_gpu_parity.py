@@ -286,6 +286,33 @@ def test_route_entry_point_on_oracle_latent(dev):
     assert np.abs(w.cpu().numpy()[~tie] - ref["w"][~tie]).max() <= 5e-5
 
 
+def test_binding_refuses_mismatched_tensors_before_launching(dev):
+    """Wrong width, dtype, layout or device of x, y, a tap or the router's
+    latent raise in the binding (no launch); the handle then still gives the
+    oracle-checked result of a correct call."""
+    wl = li.workload("tiny", tokens=17)
+    inp = li.make_inputs(wl, dev)
+    layer = layer_for(wl, inp)
+    ref = run_gpu(layer, inp.x)
+    D, R = wl.shape.hidden_size, wl.shape.moe_latent_size
+    y = torch.empty_like(inp.x)
+    with pytest.raises(ValueError, match="shape"):
+        layer.forward_into(inp.x[:, : D // 2].contiguous(), y)
+    with pytest.raises(TypeError, match="dtype"):
+        layer.forward_into(inp.x.float(), y)
+    with pytest.raises(ValueError, match="contiguous"):
+        layer.forward_into(inp.x, torch.empty(D, 17, dtype=torch.bfloat16, device=dev).t())
+    with pytest.raises(ValueError, match="GPU"):
+        layer.forward_into(inp.x.cpu(), y)
+    with pytest.raises(ValueError, match="taps.topk_idx"):
+        layer.forward_into(inp.x, y, pkg.Taps(topk_idx=torch.empty(17, 3, dtype=torch.int32,
+                                                                   device=dev)))
+    with pytest.raises(ValueError, match="shape"):
+        layer.route(torch.zeros(17, R + 1, dtype=torch.float32, device=dev))
+    again = run_gpu(layer, inp.x)
+    assert torch.equal(again.y, ref.y)
+
+
 def test_zero_tokens_is_a_noop(dev):
     wl = li.workload("tiny")
     inp = li.make_inputs(wl, dev)
