@@ -178,6 +178,9 @@ def quantize_mxfp4(w, stream=None):
     of 32), quantised along its last axis by the library's kernel:
     (codes uint8 [..., K/2], scales uint8 [..., K/32]) on w's device."""
     import torch
+    if getattr(w, "dim", lambda: 0)() < 1:
+        raise ValueError("w: expected a tensor of at least one dimension")
+    _expect(w, tuple(w.shape), torch.bfloat16, "w", contiguous=False)
     w = w.contiguous()
     K = int(w.shape[-1])
     rows = w.numel() // K if K else 0

@@ -54,3 +54,10 @@ def test_missing_or_misshapen_weights_are_refused():
     del w["router_bias"]
     with pytest.raises(ValueError, match="router_bias"):
         pkg.check_weights(sh, w)
+
+
+def test_quantiser_input_is_checked():
+    with pytest.raises(TypeError, match="dtype"):
+        pkg.quantize_mxfp4(torch.zeros(4, 32, dtype=torch.float32))
+    with pytest.raises(ValueError, match="GPU"):
+        pkg.quantize_mxfp4(torch.zeros(4, 32, dtype=torch.bfloat16))
