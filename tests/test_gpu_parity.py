@@ -216,15 +216,18 @@ def test_zero_expert_up_gives_shared_only(dev):
     del cfg
 
 
-def test_deterministic_and_token_order_equivariant(dev):
-    wl = medium(300)
+@pytest.mark.parametrize("tokens", [300, 48])
+def test_deterministic_and_token_order_equivariant(dev, tokens):
+    # T = 48: the weight-streaming projections with the shared expert's down
+    # projection on the auxiliary stream; T = 300: one concatenated GEMM
+    wl = medium(tokens)
     inp = li.make_inputs(wl, dev)
     for path in (pkg.PATH_STREAM, pkg.PATH_TILED):
         layer = layer_for(wl, inp, path)
         a = run_gpu(layer, inp.x)
         b = run_gpu(layer, inp.x)
         assert torch.equal(a.y, b.y) and np.array_equal(a.idx, b.idx)
-        perm = torch.randperm(300, generator=torch.Generator().manual_seed(4))
+        perm = torch.randperm(tokens, generator=torch.Generator().manual_seed(4))
         c = run_gpu(layer, inp.x[perm.to(dev)].contiguous())
         assert torch.equal(c.y, a.y[perm.to(dev)])
         assert np.array_equal(c.idx, a.idx[perm.numpy()])
