@@ -230,6 +230,23 @@ def near_ties(z32, wg, bias, sh, eps=1e-6):
             "eps": eps}
 
 
+def copy_calibration(torch, nbytes=4 << 30, launches=3):
+    """Read and write nbytes per launch with one elementwise kernel (int32 negation: 16-byte
+    vector loads and stores), so that a counter run over it shows what FETCH_SIZE and
+    WRITE_SIZE read for a known number of bytes."""
+    dev = torch.device("cuda:0")
+    a = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": nbytes,
+                                           "bytes_written_per_launch": nbytes,
+                                           "launches": launches,
+                                           "check": int(b[-1].item())}}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +264,10 @@ def main():
                          "layer's GEMM shapes, as a throughput yardstick (not the layer)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one captured HIP graph of the forward")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain elementwise copy of 4 GiB three times (torch.neg "
+                         "on int32), the known traffic that scales the FETCH_SIZE and "
+                         "WRITE_SIZE counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -256,6 +277,9 @@ def main():
 
     import numpy as np
     import torch
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     import lmoe_inputs as li
     import sparse_moe_layer_latentmoe_amd as pkg
 
