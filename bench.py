@@ -95,6 +95,7 @@ DECODE_SOURCES = ("gemm_stream.hip", "router.hip", "dispatch.hip", "gemm_problem
 TRAFFIC_PROFILES = {
     "decode": ("traffic_decode_T32.json", DECODE_SOURCES),
     "mtp_verify": ("traffic_mtp_verify_T192.json", DECODE_SOURCES + ("gemm_tiled.hip",)),
+    "prefill": ("traffic_prefill_T8192.json", DECODE_SOURCES + ("gemm_tiled.hip",)),
 }
 
 
@@ -384,7 +385,8 @@ def main():
     else:
         ach = sf[dom] / (stage_ms[dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(args.workload, dom),
                 "kernel": dom, "algorithmic_flops_per_launch": sf[dom],
                 "avg_launch_ms": round(stage_ms[dom], 5)}
         fl = bf16_flops(sh, T)
