@@ -42,14 +42,18 @@
  *  - arguments are checked on the host before any HIP call; on error nothing
  *    is enqueued and the status says why.  Device faults surface at the
  *    caller's next synchronisation.  Inputs must be finite.
- *  - one handle owns one workspace: do not use a handle on two streams at
- *    the same time.
- *  - the first lmoe_forward on a handle creates one auxiliary HIP stream
- *    (non-blocking, default priority) and two events, used to run the shared
- *    expert's up projection concurrently with the latent projection and the
- *    router (forked from `stream` at the start of the forward for small
- *    batches, after the latent projection otherwise, and joined back before
- *    the output projection); lmoe_destroy releases them.
+ *  - one handle owns one workspace: lmoe_forward and lmoe_route on one
+ *    handle use the same workspace (lmoe_route its router-logits part), so
+ *    calls on one handle must not overlap: issue them on one stream, or
+ *    order them with events.
+ *  - lmoe_create creates one auxiliary HIP stream (non-blocking, default
+ *    priority) and two events per handle, used to run the shared expert's up
+ *    projection concurrently with the latent projection and the router
+ *    (forked from `stream` at the start of the forward for small batches,
+ *    after the latent projection otherwise, and joined back before the
+ *    output projection); lmoe_destroy releases them.  A forward makes no
+ *    other HIP object, so any forward (the first included) can be captured
+ *    into a HIP graph.
  */
 #ifndef LMOE_H
 #define LMOE_H
@@ -144,13 +148,23 @@ typedef struct {
 
 typedef struct lmoe_handle lmoe_handle;
 
-/* Bytes of device workspace a handle with this configuration needs;
- * 0 if the configuration is invalid or unsupported. */
+/* Bytes of device workspace a handle with this configuration needs for
+ * forwards of up to cfg->max_tokens tokens: the intermediate tensors of page
+ * "Nemotron 3 Ultra 架构深度拆解报告", CH5 §5.6 Steps 1-7 (latent, router
+ * logits, top-K, the expert-sorted rows of Step 6's grouping, the experts'
+ * hidden and output rows, the weighted sum) plus the shared expert's hidden
+ * rows; layout and sizes in the library source.  0 if the configuration is
+ * invalid or unsupported.  Pure host function. */
 size_t lmoe_workspace_size(const lmoe_config *cfg);
 
-/* Validate `cfg` and `w`, carve `workspace` (device memory of at least
- * lmoe_workspace_size(cfg) bytes, 256-byte aligned, caller-owned) and
- * return a host-side handle in *out.  No HIP call is made.
+/* Set up one layer (the module of CH5 §5.6 of the page above, bound to its
+ * weights): validate `cfg` and `w` (host checks first: on any error nothing
+ * is created and *out is NULL), carve `workspace` (device memory of at
+ * least lmoe_workspace_size(cfg) bytes, 256-byte aligned, caller-owned; the
+ * library never frees it) and return a host-side handle in *out, which
+ * borrows `w` and `workspace`.  Its only HIP calls create the handle's
+ * auxiliary stream and two events on the current device (LMOE_ERR_HIP if
+ * they fail, e.g. with no GPU; nothing is left behind).
  * Debug aid: if the environment variable LMOE_DEBUG is set (and not "0")
  * when the handle is created, lmoe_forward and lmoe_route synchronise the
  * stream (and the handle's auxiliary stream) after every stage and return
@@ -186,11 +200,14 @@ lmoe_status lmoe_route(lmoe_handle *h, const float *z_f32, int32_t T, int32_t *t
 lmoe_status lmoe_quantize_mxfp4(const uint16_t *w, int64_t rows, int32_t cols, uint8_t *codes,
                                 uint8_t *scales, void *stream);
 
-/* Free the handle and the auxiliary stream and events it created (no
- * device memory is freed: the caller owns all of it).  NULL is a no-op. */
+/* Release a handle from lmoe_create: its auxiliary stream, events and any
+ * profiling events, and the host-side handle (no device memory is freed:
+ * the caller owns all of it).  Work already enqueued on the handle's
+ * streams must have finished.  NULL is a no-op. */
 void lmoe_destroy(lmoe_handle *h);
 
-/* Static text for a status code. */
+/* Static, NUL-terminated text for a status code of this header (not owned
+ * by the caller); "unknown status" for any other value.  Pure host function. */
 const char *lmoe_status_string(lmoe_status s);
 
 /* ---- per-kernel timing (HIP events on the forward's stream) ------------ */

@@ -157,6 +157,45 @@ Layout make_layout(const lmoe_config& c) {
   return L;
 }
 
+lmoe_status check_weights(const lmoe_config& c, const lmoe_weights* w) {
+  if (!w || !w->fc1_latent || !w->router || !w->router_bias || !w->fc2_latent ||
+      !w->shared_up || !w->shared_down)
+    return LMOE_ERR_INVALID_ARG;
+  const void* ptrs[6] = {w->fc1_latent, w->router,    w->router_bias,
+                         w->fc2_latent, w->shared_up, w->shared_down};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return LMOE_ERR_INVALID_ARG;
+  if (c.expert_format == LMOE_EXPERTS_MXFP4) {
+    if (!w->expert_up_mxfp4 || !w->expert_up_scale || !w->expert_down_mxfp4 ||
+        !w->expert_down_scale || !aligned16(w->expert_up_mxfp4) ||
+        !aligned16(w->expert_down_mxfp4))
+      return LMOE_ERR_INVALID_ARG;
+  } else if (!w->expert_up || !w->expert_down || !aligned16(w->expert_up) ||
+             !aligned16(w->expert_down)) {
+    return LMOE_ERR_INVALID_ARG;
+  }
+  if ((c.fuse & LMOE_FUSE_PRENORM) && (!w->norm_weight || !aligned16(w->norm_weight)))
+    return LMOE_ERR_INVALID_ARG;
+  return LMOE_OK;
+}
+
+// Host-side checks of one forward's x, y and taps.
+lmoe_status check_io(const lmoe_config& c, const uint16_t* x, int32_t T, const uint16_t* y,
+                     const lmoe_taps* taps) {
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return LMOE_ERR_INVALID_ARG;
+  const size_t xb = static_cast<size_t>(T) * c.hidden_size * 2;
+  const char* xc = reinterpret_cast<const char*>(x);
+  const char* yc = reinterpret_cast<const char*>(y);
+  if (xc < yc + xb && yc < xc + xb) return LMOE_ERR_INVALID_ARG;
+  if (taps) {
+    const void* tp[5] = {taps->z_f32, taps->topk_idx, taps->topk_w, taps->expert_counts,
+                         taps->r_latent};
+    for (const void* p : tp)
+      if (p && !aligned16(p)) return LMOE_ERR_INVALID_ARG;
+  }
+  return LMOE_OK;
+}
+
 }  // namespace
 
 struct lmoe_handle {
@@ -164,7 +203,7 @@ struct lmoe_handle {
   lmoe_weights w;
   char* ws;
   Layout L;
-  // auxiliary stream and its fork/join events, created by the first forward
+  // auxiliary stream and its fork/join events, created by lmoe_create
   hipStream_t aux = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
   // profiling
@@ -177,6 +216,197 @@ struct lmoe_handle {
   T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
 };
 
+namespace {
+
+// The launch sequence of one forward of T tokens (1 <= T <= the layout's
+// max_tokens) on the workspace `ws` carved by `L`.  `aux` (with its fork and
+// join events) runs the shared expert concurrently; without it everything
+// runs on `s`.  `ev`: profiling events of this forward, or null.
+lmoe_status run_forward(const lmoe_config& c, const lmoe_weights& w, const Layout& L, char* ws,
+                        bool debug, hipStream_t aux, hipEvent_t fork, hipEvent_t join,
+                        hipEvent_t* ev, const uint16_t* x, int32_t T, uint16_t* y, hipStream_t s,
+                        const lmoe_taps* taps) {
+  const int D = c.hidden_size, R = c.moe_latent_size, E = c.n_routed_experts;
+  const int K = c.num_experts_per_tok, F = c.moe_intermediate_size;
+  const int S = c.moe_shared_expert_intermediate_size;
+  const bool tiled_ok = tiled_dims_ok(c);
+  // Dense GEMMs: weight streaming for few tokens; LDS-tiled above that,
+  // split over k while the batch is too small to fill the GPU with tiles.
+  enum class Dense { kStream, kSplit, kTiled };
+  Dense dense = Dense::kStream;
+  if (tiled_ok && (c.path == LMOE_PATH_TILED ||
+                   (c.path == LMOE_PATH_AUTO && T > kStreamDenseMaxTokens)))
+    dense = T <= kSplitMaxTokens ? Dense::kSplit : Dense::kTiled;
+  const bool mxfp4 = c.expert_format == LMOE_EXPERTS_MXFP4;
+  const bool expert_tiled =
+      tiled_ok && (c.path == LMOE_PATH_TILED ||
+                   (c.path == LMOE_PATH_AUTO && static_cast<long>(T) * K > 32L * E));
+  const int tile_m = expert_tiled ? tiled_block_m() : kStreamTileM;
+  const int ntile_max = static_cast<int>(max_tiles(c, T, tile_m));
+
+  // Block pre-norm: the projections read bf16(gamma h) and scale by 1/rms.
+  const bool prenorm_fused = (c.fuse & LMOE_FUSE_PRENORM) != 0;
+  uint16_t* xt = reinterpret_cast<uint16_t*>(ws + L.xt);
+  float* rn = reinterpret_cast<float*>(ws + L.rn);
+  const uint16_t* xin = prenorm_fused ? xt : x;
+  const float* rscale = prenorm_fused ? rn : nullptr;
+  const uint16_t* resid = (c.fuse & LMOE_FUSE_RESIDUAL) ? x : nullptr;
+  float* z32 = reinterpret_cast<float*>(ws + L.z32);
+  uint16_t* z16 = reinterpret_cast<uint16_t*>(ws + L.z16);
+  uint16_t* hs = reinterpret_cast<uint16_t*>(ws + L.hs);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  auto proj_in = [&](const ProjIn& p, hipStream_t st) {
+    switch (dense) {
+      case Dense::kStream: return stream_proj_in(p, st);
+      case Dense::kSplit: return split_proj_in(p, part, st);
+      default: return tiled_proj_in(p, st);
+    }
+  };
+  auto proj_out = [&](const ProjOut& p, hipStream_t st) {
+    switch (dense) {
+      case Dense::kStream: return stream_proj_out(p, st);
+      case Dense::kSplit: return split_proj_out(p, part, st);
+      default: return tiled_proj_out(p, st);
+    }
+  };
+  float* logits = reinterpret_cast<float*>(ws + L.logits);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + L.idx);
+  float* tw = reinterpret_cast<float*>(ws + L.tw);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* blockcnt = reinterpret_cast<int32_t*>(ws + L.blockcnt);
+  int32_t* rows_tok = reinterpret_cast<int32_t*>(ws + L.rows_tok);
+  int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
+  Tile* tiles = reinterpret_cast<Tile*>(ws + L.tiles);
+  int32_t* ntiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
+  uint16_t* H = reinterpret_cast<uint16_t*>(ws + L.h);
+  uint16_t* O = reinterpret_cast<uint16_t*>(ws + L.o);
+  uint16_t* r16 = reinterpret_cast<uint16_t*>(ws + L.r16);
+
+  int stage = 0;
+  auto mark = [&]() -> bool {
+    if (!ev) return true;
+    return hipEventRecord(ev[stage++], s) == hipSuccess;
+  };
+  auto ok = [](hipError_t e) { return e == hipSuccess; };
+  // Debug mode: wait for the stage just launched (and the auxiliary stream)
+  // and report the first failure with the stage's name.
+  auto done = [&](const char* stage_name) -> bool {
+    if (!debug) return true;
+    hipError_t e = hipStreamSynchronize(s);
+    if (e == hipSuccess && aux) e = hipStreamSynchronize(aux);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e == hipSuccess) return true;
+    std::fprintf(stderr, "lmoe: stage %s failed: %s\n", stage_name, hipGetErrorString(e));
+    return false;
+  };
+
+  // Weight-streaming batches: the shared expert's down projection also runs
+  // on the auxiliary stream (its weight stream fills HBM time the router and
+  // dispatch leave idle), into fp32 ys; proj_out then streams only W2 and
+  // adds ys before its single rounding.
+  const bool split_out = dense == Dense::kStream && T <= kStreamDenseMaxTokens;
+  float* ys = reinterpret_cast<float*>(ws + L.ys);
+  // Shared expert's up projection on the auxiliary stream, forked from `s`
+  // at the current point and joined before proj_out.
+  // Without an auxiliary stream the same kernels run in the same order on
+  // `s`.
+  hipStream_t sh_stream = aux ? aux : s;
+  auto fork_shared = [&]() -> bool {
+    if (aux &&
+        (!ok(hipEventRecord(fork, s)) || !ok(hipStreamWaitEvent(aux, fork, 0))))
+      return false;
+    if (ev && !ok(hipEventRecord(ev[kMainStages + 1], sh_stream))) return false;
+    ProjIn pshared{xin, w.fc1_latent, w.shared_up, z32, z16, hs, T, D, R, S, R, S, rscale};
+    if (!ok(proj_in(pshared, sh_stream))) return false;
+    if (split_out) {
+      ProjOut pdown{r16, hs, w.fc2_latent, w.shared_down, y, T, D, R, S, nullptr, 1, ys};
+      if (!ok(stream_proj_out(pdown, sh_stream))) return false;
+    }
+    if (ev && !ok(hipEventRecord(ev[kMainStages + 2], sh_stream))) return false;
+    return !aux || ok(hipEventRecord(join, aux));
+  };
+  // Weight streaming: fork first, so that the shared weight stream also uses
+  // the bandwidth the short latent projection leaves idle.  Otherwise fork
+  // after the latent projection (the split-k path's partial sums are one
+  // buffer, and the tiled GEMMs would only compete for the same CUs).
+  const bool fork_first = dense == Dense::kStream;
+  if (!mark()) return LMOE_ERR_HIP;
+  if (prenorm_fused && !ok(prenorm(x, w.norm_weight, T, D, c.norm_eps, xt, rn, s)))
+    return LMOE_ERR_HIP;
+  if (prenorm_fused && !done("prenorm")) return LMOE_ERR_HIP;
+  if (fork_first && !(fork_shared() && done("shared_up"))) return LMOE_ERR_HIP;
+  ProjIn platent{xin, w.fc1_latent, w.shared_up, z32, z16, hs, T, D, R, S, 0, R, rscale};
+  if (!ok(proj_in(platent, s)) || !done("proj_latent")) return LMOE_ERR_HIP;
+  if (!fork_first && !(fork_shared() && done("shared_up"))) return LMOE_ERR_HIP;
+  if (!mark()) return LMOE_ERR_HIP;
+  if (!ok(router_logits(z32, w.router, logits, T, E, R, s)) || !done("router_logits"))
+    return LMOE_ERR_HIP;
+  if (!mark()) return LMOE_ERR_HIP;
+  if (!ok(router_select(logits, w.router_bias, T, E, R, K, c.n_group, c.topk_group,
+                        c.routed_scaling_factor, idx, tw, s)) ||
+      !done("router_select"))
+    return LMOE_ERR_HIP;
+  if (!mark()) return LMOE_ERR_HIP;
+  if (!ok(dispatch(idx, T, K, E, blockcnt, counts, offsets, rows_tok, inv, tiles, ntiles, tile_m,
+                   s)) ||
+      !done("dispatch"))
+    return LMOE_ERR_HIP;
+  if (!mark()) return LMOE_ERR_HIP;
+  if (mxfp4) {
+    ExpUpMx pup{z16, rows_tok, w.expert_up_mxfp4, w.expert_up_scale, H, R, F};
+    if (!ok(expert_tiled ? tiled_mx_exp_up(pup, tiles, ntiles, ntile_max, s)
+                         : stream_mx_exp_up(pup, tiles, ntiles, ntile_max, s)))
+      return LMOE_ERR_HIP;
+  } else {
+    ExpUp pup{z16, rows_tok, w.expert_up, H, R, F};
+    if (!ok(expert_tiled ? tiled_exp_up(pup, tiles, ntiles, ntile_max, s)
+                         : stream_exp_up(pup, tiles, ntiles, ntile_max, s)))
+      return LMOE_ERR_HIP;
+  }
+  if (!done("expert_up") || !mark()) return LMOE_ERR_HIP;
+  if (mxfp4) {
+    ExpDownMx pdn{H, w.expert_down_mxfp4, w.expert_down_scale, O, R, F};
+    if (!ok(expert_tiled ? tiled_mx_exp_down(pdn, tiles, ntiles, ntile_max, s)
+                         : stream_mx_exp_down(pdn, tiles, ntiles, ntile_max, s)))
+      return LMOE_ERR_HIP;
+  } else {
+    ExpDown pdn{H, w.expert_down, O, R, F};
+    if (!ok(expert_tiled ? tiled_exp_down(pdn, tiles, ntiles, ntile_max, s)
+                         : stream_exp_down(pdn, tiles, ntiles, ntile_max, s)))
+      return LMOE_ERR_HIP;
+  }
+  if (!done("expert_down") || !mark()) return LMOE_ERR_HIP;
+  if (!ok(combine(O, inv, tw, T, K, R, r16, taps ? taps->r_latent : nullptr, s)) ||
+      !done("combine"))
+    return LMOE_ERR_HIP;
+  if (!mark()) return LMOE_ERR_HIP;
+  // join, then y = r W2^T + Hs Wsd^T (+ h with the block residual fused)
+  if (aux && !ok(hipStreamWaitEvent(s, join, 0))) return LMOE_ERR_HIP;
+  ProjOut pout{r16, hs, w.fc2_latent, w.shared_down, y, T, D, R, S, resid,
+               split_out ? 2 : 0, ys};
+  if (!ok(proj_out(pout, s)) || !done("proj_out")) return LMOE_ERR_HIP;
+  if (!mark()) return LMOE_ERR_HIP;
+
+  if (taps) {
+    if (taps->z_f32 &&
+        !ok(hipMemcpyAsync(taps->z_f32, z32, sizeof(float) * T * R, hipMemcpyDeviceToDevice, s)))
+      return LMOE_ERR_HIP;
+    if (taps->topk_idx && !ok(hipMemcpyAsync(taps->topk_idx, idx, sizeof(int32_t) * T * K,
+                                             hipMemcpyDeviceToDevice, s)))
+      return LMOE_ERR_HIP;
+    if (taps->topk_w &&
+        !ok(hipMemcpyAsync(taps->topk_w, tw, sizeof(float) * T * K, hipMemcpyDeviceToDevice, s)))
+      return LMOE_ERR_HIP;
+    if (taps->expert_counts && !ok(hipMemcpyAsync(taps->expert_counts, counts,
+                                                  sizeof(int32_t) * E, hipMemcpyDeviceToDevice, s)))
+      return LMOE_ERR_HIP;
+  }
+  return LMOE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t lmoe_workspace_size(const lmoe_config* cfg) {
@@ -188,26 +418,10 @@ lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, void* wor
                         size_t workspace_bytes, lmoe_handle** out) {
   if (!out) return LMOE_ERR_INVALID_ARG;
   *out = nullptr;
-  const lmoe_status st = check_config(cfg);
+  lmoe_status st = check_config(cfg);
   if (st != LMOE_OK) return st;
-  if (!w || !w->fc1_latent || !w->router || !w->router_bias || !w->fc2_latent ||
-      !w->shared_up || !w->shared_down)
-    return LMOE_ERR_INVALID_ARG;
-  const void* ptrs[6] = {w->fc1_latent, w->router,    w->router_bias,
-                         w->fc2_latent, w->shared_up, w->shared_down};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return LMOE_ERR_INVALID_ARG;
-  if (cfg->expert_format == LMOE_EXPERTS_MXFP4) {
-    if (!w->expert_up_mxfp4 || !w->expert_up_scale || !w->expert_down_mxfp4 ||
-        !w->expert_down_scale || !aligned16(w->expert_up_mxfp4) ||
-        !aligned16(w->expert_down_mxfp4))
-      return LMOE_ERR_INVALID_ARG;
-  } else if (!w->expert_up || !w->expert_down || !aligned16(w->expert_up) ||
-             !aligned16(w->expert_down)) {
-    return LMOE_ERR_INVALID_ARG;
-  }
-  if ((cfg->fuse & LMOE_FUSE_PRENORM) && (!w->norm_weight || !aligned16(w->norm_weight)))
-    return LMOE_ERR_INVALID_ARG;
+  st = check_weights(*cfg, w);
+  if (st != LMOE_OK) return st;
   const Layout L = make_layout(*cfg);
   if (!workspace || workspace_bytes < L.total) return LMOE_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return LMOE_ERR_WORKSPACE;
@@ -219,6 +433,14 @@ lmoe_status lmoe_create(const lmoe_config* cfg, const lmoe_weights* w, void* wor
   h->L = L;
   const char* dbg = std::getenv("LMOE_DEBUG");
   h->debug = dbg && *dbg && std::strcmp(dbg, "0") != 0;
+  // The auxiliary stream and its fork/join events, created here so that
+  // every lmoe_forward (the first included) can be captured into a graph.
+  if (hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->join, hipEventDisableTiming) != hipSuccess) {
+    lmoe_destroy(h);
+    return LMOE_ERR_HIP;
+  }
   *out = h;
   return LMOE_OK;
 }
@@ -341,202 +563,13 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
   if (T < 0) return LMOE_ERR_INVALID_ARG;
   if (T > h->cfg.max_tokens) return LMOE_ERR_TOO_MANY_TOKENS;
   if (T == 0) return LMOE_OK;
-  const lmoe_config& c = h->cfg;
-  const int D = c.hidden_size, R = c.moe_latent_size, E = c.n_routed_experts;
-  const int K = c.num_experts_per_tok, F = c.moe_intermediate_size;
-  const int S = c.moe_shared_expert_intermediate_size;
-  if (!x || !y || !aligned16(x) || !aligned16(y)) return LMOE_ERR_INVALID_ARG;
-  const size_t xb = static_cast<size_t>(T) * D * 2;
-  const char* xc = reinterpret_cast<const char*>(x);
-  const char* yc = reinterpret_cast<const char*>(y);
-  if (xc < yc + xb && yc < xc + xb) return LMOE_ERR_INVALID_ARG;
-  if (taps) {
-    const void* tp[5] = {taps->z_f32, taps->topk_idx, taps->topk_w, taps->expert_counts,
-                         taps->r_latent};
-    for (const void* p : tp)
-      if (p && !aligned16(p)) return LMOE_ERR_INVALID_ARG;
-  }
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool tiled_ok = tiled_dims_ok(c);
-  // Dense GEMMs: weight streaming for few tokens; LDS-tiled above that,
-  // split over k while the batch is too small to fill the GPU with tiles.
-  enum class Dense { kStream, kSplit, kTiled };
-  Dense dense = Dense::kStream;
-  if (tiled_ok && (c.path == LMOE_PATH_TILED ||
-                   (c.path == LMOE_PATH_AUTO && T > kStreamDenseMaxTokens)))
-    dense = T <= kSplitMaxTokens ? Dense::kSplit : Dense::kTiled;
-  const bool mxfp4 = c.expert_format == LMOE_EXPERTS_MXFP4;
-  const bool expert_tiled =
-      tiled_ok && (c.path == LMOE_PATH_TILED ||
-                   (c.path == LMOE_PATH_AUTO && static_cast<long>(T) * K > 32L * E));
-  const int tile_m = expert_tiled ? tiled_block_m() : kStreamTileM;
-  const int ntile_max = static_cast<int>(max_tiles(c, T, tile_m));
-
-  // Block pre-norm: the projections read bf16(gamma h) and scale by 1/rms.
-  const bool prenorm_fused = (c.fuse & LMOE_FUSE_PRENORM) != 0;
-  uint16_t* xt = h->at<uint16_t>(h->L.xt);
-  float* rn = h->at<float>(h->L.rn);
-  const uint16_t* xin = prenorm_fused ? xt : x;
-  const float* rscale = prenorm_fused ? rn : nullptr;
-  const uint16_t* resid = (c.fuse & LMOE_FUSE_RESIDUAL) ? x : nullptr;
-  float* z32 = h->at<float>(h->L.z32);
-  uint16_t* z16 = h->at<uint16_t>(h->L.z16);
-  uint16_t* hs = h->at<uint16_t>(h->L.hs);
-  float* part = h->at<float>(h->L.part);
-  auto proj_in = [&](const ProjIn& p, hipStream_t st) {
-    switch (dense) {
-      case Dense::kStream: return stream_proj_in(p, st);
-      case Dense::kSplit: return split_proj_in(p, part, st);
-      default: return tiled_proj_in(p, st);
-    }
-  };
-  auto proj_out = [&](const ProjOut& p, hipStream_t st) {
-    switch (dense) {
-      case Dense::kStream: return stream_proj_out(p, st);
-      case Dense::kSplit: return split_proj_out(p, part, st);
-      default: return tiled_proj_out(p, st);
-    }
-  };
-  float* logits = h->at<float>(h->L.logits);
-  int32_t* idx = h->at<int32_t>(h->L.idx);
-  float* tw = h->at<float>(h->L.tw);
-  int32_t* counts = h->at<int32_t>(h->L.counts);
-  int32_t* offsets = h->at<int32_t>(h->L.offsets);
-  int32_t* blockcnt = h->at<int32_t>(h->L.blockcnt);
-  int32_t* rows_tok = h->at<int32_t>(h->L.rows_tok);
-  int32_t* inv = h->at<int32_t>(h->L.inv);
-  Tile* tiles = h->at<Tile>(h->L.tiles);
-  int32_t* ntiles = h->at<int32_t>(h->L.ntiles);
-  uint16_t* H = h->at<uint16_t>(h->L.h);
-  uint16_t* O = h->at<uint16_t>(h->L.o);
-  uint16_t* r16 = h->at<uint16_t>(h->L.r16);
-
-  if (!h->aux) {
-    if (hipStreamCreateWithFlags(&h->aux, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&h->join, hipEventDisableTiming) != hipSuccess)
-      return LMOE_ERR_HIP;
-  }
+  const lmoe_status st = check_io(h->cfg, x, T, y, taps);
+  if (st != LMOE_OK) return st;
   hipEvent_t* ev = nullptr;
   if (h->prof_n < h->prof_max)
     ev = &h->events[static_cast<size_t>(h->prof_n++) * kEventsPerForward];
-  int stage = 0;
-  auto mark = [&]() -> bool {
-    if (!ev) return true;
-    return hipEventRecord(ev[stage++], s) == hipSuccess;
-  };
-  auto ok = [](hipError_t e) { return e == hipSuccess; };
-  // Debug mode: wait for the stage just launched (and the auxiliary stream)
-  // and report the first failure with the stage's name.
-  auto done = [&](const char* stage_name) -> bool {
-    if (!h->debug) return true;
-    hipError_t e = hipStreamSynchronize(s);
-    if (e == hipSuccess && h->aux) e = hipStreamSynchronize(h->aux);
-    if (e == hipSuccess) e = hipGetLastError();
-    if (e == hipSuccess) return true;
-    std::fprintf(stderr, "lmoe: stage %s failed: %s\n", stage_name, hipGetErrorString(e));
-    return false;
-  };
-
-  // Weight-streaming batches: the shared expert's down projection also runs
-  // on the auxiliary stream (its weight stream fills HBM time the router and
-  // dispatch leave idle), into fp32 ys; proj_out then streams only W2 and
-  // adds ys before its single rounding.
-  const bool split_out = dense == Dense::kStream && T <= kStreamDenseMaxTokens;
-  float* ys = h->at<float>(h->L.ys);
-  // Shared expert's up projection on the auxiliary stream, forked from `s`
-  // at the current point and joined before proj_out.
-  auto fork_shared = [&]() -> bool {
-    if (!ok(hipEventRecord(h->fork, s)) || !ok(hipStreamWaitEvent(h->aux, h->fork, 0)))
-      return false;
-    if (ev && !ok(hipEventRecord(ev[kMainStages + 1], h->aux))) return false;
-    ProjIn pshared{xin, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, R, S, rscale};
-    if (!ok(proj_in(pshared, h->aux))) return false;
-    if (split_out) {
-      ProjOut pdown{r16, hs, h->w.fc2_latent, h->w.shared_down, y, T, D, R, S, nullptr, 1, ys};
-      if (!ok(stream_proj_out(pdown, h->aux))) return false;
-    }
-    if (ev && !ok(hipEventRecord(ev[kMainStages + 2], h->aux))) return false;
-    return ok(hipEventRecord(h->join, h->aux));
-  };
-  // Weight streaming: fork first, so that the shared weight stream also uses
-  // the bandwidth the short latent projection leaves idle.  Otherwise fork
-  // after the latent projection (the split-k path's partial sums are one
-  // buffer, and the tiled GEMMs would only compete for the same CUs).
-  const bool fork_first = dense == Dense::kStream;
-  if (!mark()) return LMOE_ERR_HIP;
-  if (prenorm_fused && !ok(prenorm(x, h->w.norm_weight, T, D, c.norm_eps, xt, rn, s)))
-    return LMOE_ERR_HIP;
-  if (prenorm_fused && !done("prenorm")) return LMOE_ERR_HIP;
-  if (fork_first && !(fork_shared() && done("shared_up"))) return LMOE_ERR_HIP;
-  ProjIn platent{xin, h->w.fc1_latent, h->w.shared_up, z32, z16, hs, T, D, R, S, 0, R, rscale};
-  if (!ok(proj_in(platent, s)) || !done("proj_latent")) return LMOE_ERR_HIP;
-  if (!fork_first && !(fork_shared() && done("shared_up"))) return LMOE_ERR_HIP;
-  if (!mark()) return LMOE_ERR_HIP;
-  if (!ok(router_logits(z32, h->w.router, logits, T, E, R, s)) || !done("router_logits"))
-    return LMOE_ERR_HIP;
-  if (!mark()) return LMOE_ERR_HIP;
-  if (!ok(router_select(logits, h->w.router_bias, T, E, R, K, c.n_group, c.topk_group,
-                        c.routed_scaling_factor, idx, tw, s)) ||
-      !done("router_select"))
-    return LMOE_ERR_HIP;
-  if (!mark()) return LMOE_ERR_HIP;
-  if (!ok(dispatch(idx, T, K, E, blockcnt, counts, offsets, rows_tok, inv, tiles, ntiles, tile_m,
-                   s)) ||
-      !done("dispatch"))
-    return LMOE_ERR_HIP;
-  if (!mark()) return LMOE_ERR_HIP;
-  if (mxfp4) {
-    ExpUpMx pup{z16, rows_tok, h->w.expert_up_mxfp4, h->w.expert_up_scale, H, R, F};
-    if (!ok(expert_tiled ? tiled_mx_exp_up(pup, tiles, ntiles, ntile_max, s)
-                         : stream_mx_exp_up(pup, tiles, ntiles, ntile_max, s)))
-      return LMOE_ERR_HIP;
-  } else {
-    ExpUp pup{z16, rows_tok, h->w.expert_up, H, R, F};
-    if (!ok(expert_tiled ? tiled_exp_up(pup, tiles, ntiles, ntile_max, s)
-                         : stream_exp_up(pup, tiles, ntiles, ntile_max, s)))
-      return LMOE_ERR_HIP;
-  }
-  if (!done("expert_up") || !mark()) return LMOE_ERR_HIP;
-  if (mxfp4) {
-    ExpDownMx pdn{H, h->w.expert_down_mxfp4, h->w.expert_down_scale, O, R, F};
-    if (!ok(expert_tiled ? tiled_mx_exp_down(pdn, tiles, ntiles, ntile_max, s)
-                         : stream_mx_exp_down(pdn, tiles, ntiles, ntile_max, s)))
-      return LMOE_ERR_HIP;
-  } else {
-    ExpDown pdn{H, h->w.expert_down, O, R, F};
-    if (!ok(expert_tiled ? tiled_exp_down(pdn, tiles, ntiles, ntile_max, s)
-                         : stream_exp_down(pdn, tiles, ntiles, ntile_max, s)))
-      return LMOE_ERR_HIP;
-  }
-  if (!done("expert_down") || !mark()) return LMOE_ERR_HIP;
-  if (!ok(combine(O, inv, tw, T, K, R, r16, taps ? taps->r_latent : nullptr, s)) ||
-      !done("combine"))
-    return LMOE_ERR_HIP;
-  if (!mark()) return LMOE_ERR_HIP;
-  // join, then y = r W2^T + Hs Wsd^T (+ h with the block residual fused)
-  if (!ok(hipStreamWaitEvent(s, h->join, 0))) return LMOE_ERR_HIP;
-  ProjOut pout{r16, hs, h->w.fc2_latent, h->w.shared_down, y, T, D, R, S, resid,
-               split_out ? 2 : 0, ys};
-  if (!ok(proj_out(pout, s)) || !done("proj_out")) return LMOE_ERR_HIP;
-  if (!mark()) return LMOE_ERR_HIP;
-
-  if (taps) {
-    if (taps->z_f32 &&
-        !ok(hipMemcpyAsync(taps->z_f32, z32, sizeof(float) * T * R, hipMemcpyDeviceToDevice, s)))
-      return LMOE_ERR_HIP;
-    if (taps->topk_idx && !ok(hipMemcpyAsync(taps->topk_idx, idx, sizeof(int32_t) * T * K,
-                                             hipMemcpyDeviceToDevice, s)))
-      return LMOE_ERR_HIP;
-    if (taps->topk_w &&
-        !ok(hipMemcpyAsync(taps->topk_w, tw, sizeof(float) * T * K, hipMemcpyDeviceToDevice, s)))
-      return LMOE_ERR_HIP;
-    if (taps->expert_counts && !ok(hipMemcpyAsync(taps->expert_counts, counts,
-                                                  sizeof(int32_t) * E, hipMemcpyDeviceToDevice, s)))
-      return LMOE_ERR_HIP;
-  }
-  return LMOE_OK;
+  return run_forward(h->cfg, h->w, h->L, h->ws, h->debug, h->aux, h->fork, h->join, ev, x, T, y,
+                     static_cast<hipStream_t>(stream), taps);
 }
 
 }  // extern "C"

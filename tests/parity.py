@@ -129,6 +129,57 @@ def compare(g: GpuRun, x_bits: np.ndarray, hw, sh, rows=None, block: Block | Non
     )
 
 
+@dataclass
+class RoutingReport:
+    """Every token's selection against the oracle's (Steps 1-3 on the
+    oracle's own latent of the whole batch)."""
+    tokens: int
+    ties: int                  # tokens whose oracle K-th / (K+1)-th gap < TIE_GAP
+    tie_rows: np.ndarray       # their row numbers
+    ties_routed_differently: int
+    mismatched: int            # non-tie tokens whose selection differs
+    min_gap: float
+    rel_z: float               # GPU fp32 latent vs the oracle's, normwise, all rows
+    max_w_err: float           # GPU weights vs the oracle's on the GPU's selection
+
+    def __str__(self):
+        return (f"routing of all {self.tokens} tokens: {self.mismatched} non-tie mismatches, "
+                f"{self.ties} ties (rows {self.tie_rows.tolist()}, "
+                f"{self.ties_routed_differently} routed differently), min gap "
+                f"{self.min_gap:.3e}, latent rel {self.rel_z:.2e}, max |dw| {self.max_w_err:.2e}")
+
+
+def route_every_token(g: GpuRun, x_bits: np.ndarray, hw, sh,
+                      block: Block | None = None) -> RoutingReport:
+    """The oracle's latent projection, router scores and top-K for every row
+    of the batch (no sampling), compared with the GPU's selections."""
+    cfg = oracle_config(sh)
+    if block is not None and block.gamma_bits is not None:
+        xt, rn = O.rms_prenorm(x_bits, block.gamma_bits, block.eps)
+        xin = rn[:, None] * O.bf16_bits_to_f64(xt)
+    else:
+        xin = O.bf16_bits_to_f64(x_bits)
+    z32 = O.latent_projection(xin, O.bf16_bits_to_f64(hw.fc1_latent)).astype(np.float32)
+    del xin
+    _, s = O.router_scores(z32, hw.router)
+    idx, _, gap = O.select_experts(s, hw.router_bias, cfg.num_experts_per_tok, cfg.n_group,
+                                   cfg.topk_group)
+    tie = gap < TIE_GAP
+    same = np.all(g.idx == idx, axis=1)
+    w = O.renormalize(s, g.idx, cfg.routed_scaling_factor)
+    return RoutingReport(
+        tokens=int(x_bits.shape[0]), ties=int(tie.sum()), tie_rows=np.nonzero(tie)[0],
+        ties_routed_differently=int((tie & ~same).sum()), mismatched=int((~same & ~tie).sum()),
+        min_gap=float(gap.min()), rel_z=normwise_rel(g.z32, z32),
+        max_w_err=float(np.abs(g.w.astype(np.float64) - w).max()))
+
+
+def assert_routing(rep: RoutingReport) -> None:
+    assert rep.mismatched == 0, f"{rep.mismatched} non-tie tokens routed differently: {rep}"
+    assert rep.rel_z <= 1e-5, rep
+    assert rep.max_w_err <= 5e-5, rep
+
+
 class MxfpExperts:
     """``obj[e]``: expert e's weights as the oracle quantises them to MXFP4
     and back (float64), from the bf16 bits of ``src[e]``; cached, with the

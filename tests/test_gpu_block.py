@@ -12,8 +12,8 @@ import torch
 
 import lmoe_inputs as li
 import sparse_moe_layer_latentmoe_amd as pkg
-from parity import (MEDIUM, Block, assert_parity, check_properties, compare,
-                    mxfp4_host_weights, run_gpu, weight_dict)
+from parity import (MEDIUM, Block, assert_parity, assert_routing, check_properties, compare,
+                    mxfp4_host_weights, route_every_token, run_gpu, weight_dict)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,11 +57,19 @@ def run_block(dev, shape, tokens, fuse, path=pkg.PATH_AUTO, eps=1e-5, rows=None,
     check_properties(g, shape, tokens)
     block = Block(li.bf16_bits(gamma) if fuse & pkg.FUSE_PRENORM else None, eps,
                   bool(fuse & pkg.FUSE_RESIDUAL))
+    x_bits = li.bf16_bits(inp.x)
+    if rows is not None:
+        # sampled outputs: every token's routing against the oracle's, and
+        # the tie tokens added to the rows whose whole output is compared
+        routing = route_every_token(g, x_bits, hw, shape, block=block)
+        say(f"  {routing}")
+        assert_routing(routing)
+        rows = np.union1d(rows, routing.tie_rows)
     if rows is not None and expert_format == pkg.EXPERTS_MXFP4:
         used = np.unique(g.idx[rows])
         hw.expert_up.prefetch(used)
         hw.expert_down.prefetch(used)
-    rep = compare(g, li.bf16_bits(inp.x), hw, shape, rows=rows, block=block)
+    rep = compare(g, x_bits, hw, shape, rows=rows, block=block)
     say(f"  {rep}")
     assert_parity(rep)
     return g, inp
@@ -121,7 +129,8 @@ def test_block_output_is_residual_plus_layer(dev):
 
 @pytest.mark.fullshape
 def test_block_decode_full_shape(dev):
-    """Decode batch at full shape with both block steps fused: properties on
-    every token, the oracle on three sampled tokens."""
+    """Decode batch at full shape with both block steps fused: properties and
+    routing on every token, the whole output on three sampled tokens (and
+    any tie token)."""
     wl = li.workload("decode")
     run_block(dev, wl.shape, wl.tokens, BOTH, rows=np.array([0, 17, wl.tokens - 1]), wl=wl)

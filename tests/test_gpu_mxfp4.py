@@ -12,8 +12,8 @@ import torch
 
 import lmoe_inputs as li
 import sparse_moe_layer_latentmoe_amd as pkg
-from parity import (MEDIUM, assert_parity, check_properties, compare, medium,
-                    mxfp4_host_weights, run_gpu, weight_dict)
+from parity import (MEDIUM, assert_parity, assert_routing, check_properties, compare, medium,
+                    mxfp4_host_weights, route_every_token, run_gpu, weight_dict)
 from oracle import lmoe_oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -129,8 +129,9 @@ def test_mxfp4_forward_matches_oracle(dev, shape, tokens, path):
 def test_mxfp4_full_shape(dev, name, rows):
     """The decode batch (weight streaming) and the prefill batch (LDS-tiled
     MXFP4 GEMMs) at full shape with MXFP4 experts: properties on every
-    token, the oracle on three sampled tokens (every expert they use
-    quantised by the oracle and compared with the library's codes)."""
+    token, every token's routing against the oracle's, the whole output on
+    three sampled tokens plus any tie token (every expert they use quantised
+    by the oracle and compared with the library's codes)."""
     wl = li.workload(name)
     say(f"[mxfp4 full {name}]")
     inp = li.make_inputs(wl, dev)
@@ -138,15 +139,19 @@ def test_mxfp4_full_shape(dev, name, rows):
     layer = pkg.LatentMoE(wl.shape, w, wl.tokens, expert_format=pkg.EXPERTS_MXFP4)
     g = run_gpu(layer, inp.x)
     check_properties(g, wl.shape, wl.tokens)
-    rows = np.array(rows)
     # the oracle quantises the touched experts itself, from the bf16 weights
     hw = mxfp4_host_weights(inp)
+    x_bits = li.bf16_bits(inp.x)
+    routing = route_every_token(g, x_bits, hw, wl.shape)
+    say(f"  {routing}")
+    assert_routing(routing)
+    rows = np.union1d(np.array(rows), routing.tie_rows)
     used = np.unique(g.idx[rows])
     hw.expert_up.prefetch(used)
     hw.expert_down.prefetch(used)
     for e in used:
         assert np.array_equal(w["expert_up_mxfp4"][int(e)].cpu().numpy(), hw.expert_up.coded[int(e)][0])
         assert np.array_equal(w["expert_down_scale"][int(e)].cpu().numpy(), hw.expert_down.coded[int(e)][1])
-    rep = compare(g, li.bf16_bits(inp.x), hw, wl.shape, rows=rows)
-    say(f"  sampled rows {rows.tolist()}: {rep}")
+    rep = compare(g, x_bits, hw, wl.shape, rows=rows)
+    say(f"  sampled and tie rows {rows.tolist()}: {rep}")
     assert_parity(rep)
