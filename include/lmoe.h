@@ -71,7 +71,9 @@ typedef enum {
   LMOE_ERR_UNSUPPORTED = -2,     /* a configuration this library does not implement */
   LMOE_ERR_TOO_MANY_TOKENS = -3, /* T > max_tokens of the handle */
   LMOE_ERR_WORKSPACE = -4,       /* workspace missing or smaller than lmoe_workspace_size */
-  LMOE_ERR_HIP = -5              /* a HIP launch or copy returned an error */
+  LMOE_ERR_HIP = -5,             /* a HIP launch or copy returned an error */
+  LMOE_ERR_SCRATCH = -6          /* lmoe_forward_noalloc: the forward needs more than
+                                    LMOE_NOALLOC_SCRATCH_BYTES of scratch */
 } lmoe_status;
 
 /* Path selection for the expert and projection GEMMs.  AUTO picks by token
@@ -209,6 +211,28 @@ void lmoe_destroy(lmoe_handle *h);
 /* Static, NUL-terminated text for a status code of this header (not owned
  * by the caller); "unknown status" for any other value.  Pure host function. */
 const char *lmoe_status_string(lmoe_status s);
+
+/* ---- allocation-free forward --------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward as lmoe_forward (same kernels, same results bit for bit) without a
+ * handle or a workspace.  Its scratch (the workspace a handle for exactly T
+ * tokens would need) lives in one static device array of
+ * LMOE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends; at the full layer shape (hidden 8192, latent
+ * 2048, 512 experts top-22) that covers up to about 90 tokens, e.g. the
+ * 32-token decode batch.  Larger forwards return LMOE_ERR_SCRATCH before any
+ * launch.  Nothing is allocated and no stream or event is created: the
+ * shared expert runs on `stream` after the others.  The first call on a
+ * device looks up the array's address there (make it outside graph
+ * capture).  `cfg` and `w` are checked as by lmoe_create, x and y as by
+ * lmoe_forward; T <= cfg->max_tokens; `stream` must belong to the current
+ * device.  Every call on one GPU uses that GPU's one array (it keeps the
+ * last call's contents; nothing in it needs clearing): calls that overlap
+ * on one GPU, on any streams, race and give wrong results. */
+#define LMOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+lmoe_status lmoe_forward_noalloc(const lmoe_config *cfg, const lmoe_weights *w,
+                                 const uint16_t *x, int32_t T, uint16_t *y, void *stream);
 
 /* ---- per-kernel timing (HIP events on the forward's stream) ------------ */
 

@@ -25,6 +25,8 @@ LMOE_ERR_UNSUPPORTED = -2
 LMOE_ERR_TOO_MANY_TOKENS = -3
 LMOE_ERR_WORKSPACE = -4
 LMOE_ERR_HIP = -5
+LMOE_ERR_SCRATCH = -6
+NOALLOC_SCRATCH_BYTES = 64 << 20      # LMOE_NOALLOC_SCRATCH_BYTES
 
 PATH_AUTO, PATH_STREAM, PATH_TILED = 0, 1, 2
 EXPERTS_BF16, EXPERTS_MXFP4 = 0, 1
@@ -34,7 +36,7 @@ FUSE_BLOCK = FUSE_PRENORM | FUSE_RESIDUAL
 EXPORTED = (
     "lmoe_workspace_size", "lmoe_create", "lmoe_forward", "lmoe_route", "lmoe_destroy",
     "lmoe_status_string", "lmoe_num_stages", "lmoe_stage_name", "lmoe_profile_begin",
-    "lmoe_profile_end", "lmoe_quantize_mxfp4",
+    "lmoe_profile_end", "lmoe_quantize_mxfp4", "lmoe_forward_noalloc",
 )
 
 
@@ -118,6 +120,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lmoe_profile_end.restype = ctypes.c_int
     lib.lmoe_quantize_mxfp4.argtypes = [P, ctypes.c_int64, ctypes.c_int32, P, P, P]
     lib.lmoe_quantize_mxfp4.restype = ctypes.c_int
+    lib.lmoe_forward_noalloc.argtypes = [ctypes.POINTER(LmoeConfig), ctypes.POINTER(LmoeWeights),
+                                         P, ctypes.c_int32, P, P]
+    lib.lmoe_forward_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -322,6 +327,21 @@ class LatentMoE:
                                    ctypes.byref(ts) if ts is not None else None)
         if st != LMOE_OK:
             raise LmoeError(st, "lmoe_forward")
+
+    def forward_noalloc_into(self, x, y, stream=None) -> None:
+        """y <- LatentMoE(x) through lmoe_forward_noalloc: the same forward
+        without the handle's workspace or auxiliary stream, its scratch in the
+        library's static device array (raises LmoeError with LMOE_ERR_SCRATCH
+        when T tokens need more than NOALLOC_SCRATCH_BYTES)."""
+        import torch
+        sh = self.shape
+        T = int(x.shape[0]) if getattr(x, "dim", lambda: 0)() == 2 else -1
+        _expect(x, (T, sh.hidden_size), torch.bfloat16, "x", device=self.device)
+        _expect(y, (T, sh.hidden_size), torch.bfloat16, "y", device=self.device)
+        st = self.lib.lmoe_forward_noalloc(ctypes.byref(self.cfg), ctypes.byref(self.wstruct),
+                                           _ptr(x), T, _ptr(y), _stream_handle(stream))
+        if st != LMOE_OK:
+            raise LmoeError(st, "lmoe_forward_noalloc")
 
     def forward(self, x, taps: Taps | None = None, stream=None):
         import torch

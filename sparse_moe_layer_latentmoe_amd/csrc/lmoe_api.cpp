@@ -28,6 +28,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -405,6 +406,34 @@ lmoe_status run_forward(const lmoe_config& c, const lmoe_weights& w, const Layou
   return LMOE_OK;
 }
 
+// Scratch of the allocation-free forward: one static device array, which
+// every GPU the library runs on holds (its own copy, at its own address)
+// until the process ends.  Host code never passes `scratch` itself to a
+// kernel (on the host it names a host-side stand-in); it looks up the
+// device address once per device and keeps it.
+constexpr size_t kScratchBytes = LMOE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device, with that device current).
+lmoe_status device_scratch(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return LMOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return LMOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return LMOE_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return LMOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -462,6 +491,7 @@ const char* lmoe_status_string(lmoe_status s) {
     case LMOE_ERR_TOO_MANY_TOKENS: return "token count exceeds max_tokens";
     case LMOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case LMOE_ERR_HIP: return "HIP runtime error";
+    case LMOE_ERR_SCRATCH: return "input too large for the allocation-free forward's scratch";
   }
   return "unknown status";
 }
@@ -570,6 +600,38 @@ lmoe_status lmoe_forward(lmoe_handle* h, const uint16_t* x, int32_t T, uint16_t*
     ev = &h->events[static_cast<size_t>(h->prof_n++) * kEventsPerForward];
   return run_forward(h->cfg, h->w, h->L, h->ws, h->debug, h->aux, h->fork, h->join, ev, x, T, y,
                      static_cast<hipStream_t>(stream), taps);
+}
+
+lmoe_status lmoe_forward_noalloc(const lmoe_config* cfg, const lmoe_weights* w,
+                                 const uint16_t* x, int32_t T, uint16_t* y, void* stream) {
+  lmoe_status st = check_config(cfg);
+  if (st != LMOE_OK) return st;
+  st = check_weights(*cfg, w);
+  if (st != LMOE_OK) return st;
+  if (T < 0) return LMOE_ERR_INVALID_ARG;
+  if (T > cfg->max_tokens) return LMOE_ERR_TOO_MANY_TOKENS;
+  if (T == 0) return LMOE_OK;
+  st = check_io(*cfg, x, T, y, nullptr);
+  if (st != LMOE_OK) return st;
+  // the workspace of a handle made for exactly T tokens, carved from the
+  // static scratch instead of caller memory
+  lmoe_config c = *cfg;
+  c.max_tokens = T;
+  const Layout L = make_layout(c);
+  if (L.total > kScratchBytes) return LMOE_ERR_SCRATCH;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int cur = -1, sdev = -1;
+  if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(s, &sdev) != hipSuccess)
+    return LMOE_ERR_HIP;
+  if (sdev != cur) return LMOE_ERR_INVALID_ARG;
+  char* ws = nullptr;
+  st = device_scratch(&ws);
+  if (st != LMOE_OK) return st;
+  // Every scratch byte a forward reads is written earlier in the same
+  // forward (LDS-only atomics, no accumulation into device memory), so
+  // nothing is cleared first.  One stream: no auxiliary stream or event.
+  return run_forward(c, *w, L, ws, false, nullptr, nullptr, nullptr, nullptr, x, T, y, s,
+                     nullptr);
 }
 
 }  // extern "C"

@@ -221,8 +221,37 @@ def test_forward_and_route_argument_errors(lib):
     lib.lmoe_destroy(h)
 
 
+def test_noalloc_forward_argument_errors(lib):
+    """lmoe_forward_noalloc checks cfg, weights, T, x and y on the host, and
+    rejects a forward whose scratch exceeds the static array, before any HIP
+    call (the full-shape layer at T = 192 needs ~130 MB against 64 MiB)."""
+    f = lib.lmoe_forward_noalloc
+    c = cfg()
+    w = weights()
+    D = c.hidden_size
+    x, y = FAKE, FAKE + 64 * D * 2 + 4096
+    assert f(None, ctypes.byref(w), x, 4, y, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(cfg(path=7)), ctypes.byref(w), x, 4, y, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(c), None, x, 4, y, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(c), ctypes.byref(weights(router=None)), x, 4, y,
+             None) == pkg.LMOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(c), ctypes.byref(w), x, -1, y, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(c), ctypes.byref(w), x, 65, y, None) == pkg.LMOE_ERR_TOO_MANY_TOKENS
+    assert f(ctypes.byref(c), ctypes.byref(w), x, 0, y, None) == pkg.LMOE_OK   # no-op
+    assert f(ctypes.byref(c), ctypes.byref(w), None, 4, y, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(c), ctypes.byref(w), x + 2, 4, y, None) == pkg.LMOE_ERR_INVALID_ARG
+    assert f(ctypes.byref(c), ctypes.byref(w), x, 4, x + 2 * D, None) == pkg.LMOE_ERR_INVALID_ARG
+    full = pkg.make_config(li.FULL, 256)
+    fx, fy = FAKE, FAKE + (1 << 30)
+    assert f(ctypes.byref(full), ctypes.byref(w), fx, 192, fy, None) == pkg.LMOE_ERR_SCRATCH
+    # the limit is the workspace a handle for exactly T tokens would need
+    for T, fits in ((32, True), (192, False)):
+        need = lib.lmoe_workspace_size(ctypes.byref(pkg.make_config(li.FULL, T)))
+        assert (need <= pkg.NOALLOC_SCRATCH_BYTES) == fits
+
+
 def test_status_strings_and_stages(lib):
-    for s in (0, -1, -2, -3, -4, -5):
+    for s in (0, -1, -2, -3, -4, -5, -6):
         assert lib.lmoe_status_string(s)
     assert lib.lmoe_status_string(99) == b"unknown status"
     names = pkg.stage_names()
