@@ -270,6 +270,306 @@ __global__ __launch_bounds__(128 * WGN) void tiled_gemm_kernel(P p, int mrows, c
     }
 }
 
+// ---- Two-stage LDS GEMM with scalar addressing -----------------------------
+//
+// The same tiling and results as tiled_gemm_kernel with NS = 2 (eight waves,
+// 2 along tokens x 4 along weights, BK = 64, both operands copied global ->
+// LDS with 16-byte direct loads, the same swizzle, the same MFMA order, so
+// the outputs are bit for bit those of tiled_gemm_kernel), written so that
+// the compiler sees what is uniform:
+//  - the wave index, the tile's row count and its expert are read into
+//    scalar registers (readfirstlane), so the per-wave "rows left" tests are
+//    scalar branches, not exec-mask regions (inside those regions the
+//    compiler had waited for every LDS read before the first MFMA);
+//  - copies are buffer loads: a per-lane 32-bit offset (fixed for the whole
+//    tile) plus the k offset in a scalar register, so a k step costs no
+//    vector address arithmetic;
+//  - the k loop is unrolled over the two stage buffers, so every LDS address
+//    is a register plus an immediate, and its last step is peeled (no copy);
+//  - a wave whose token rows all lie past the tile's count only copies.
+// Measured on the prefill batch's problems (standalone, same inputs): expert
+// up 4.60 -> 4.43 ms, shared up 1.13 -> 1.03 ms (with the directed MFMA /
+// LDS-read interleave, SCHED = 1); expert down 4.50 -> 4.60 ms, so the down
+// projection keeps tiled_gemm_kernel.  Launched when the k range is an even
+// number of 64-wide k tiles (every full-shape problem).
+
+// Problems whose k range has two segments (the output projection's [r | Hs]).
+template <class P>
+struct TwoSegments : std::false_type {};
+template <>
+struct TwoSegments<ProjOut> : std::true_type {};
+template <>
+struct TwoSegments<SplitK<ProjOut>> : std::true_type {};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base) {
+  // raw buffer over 2 GiB from `base`: offsets are checked against this
+  // bound by the hardware (reads past it return 0)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFF0,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// A barrier that is also a hard scheduling boundary: no LDS read of the
+// stage may be hoisted above it (its data is not there yet) and no read of
+// the previous stage sunk below it (other waves overwrite that buffer next).
+__device__ __forceinline__ void stage_barrier_hard() {
+  __builtin_amdgcn_sched_barrier(0);
+  stage_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// work_item with the tile list's fields read into scalar registers.
+template <bool GROUPED>
+__device__ __forceinline__ bool work_item_uniform(int nblocks, int mrows, int bm,
+                                                  const Tile* tiles, const int* ntiles, int& tm,
+                                                  int& nb) {
+  const int mtiles = GROUPED ? uniform(*ntiles) : (mrows + bm - 1) / bm;
+  const int total = mtiles * nblocks;
+  const int chunk = (total + kXcds - 1) / kXcds;
+  const int local = blockIdx.x / kXcds;
+  const int item = (blockIdx.x % kXcds) * chunk + local;
+  if (local >= chunk || item >= total) return false;
+  if (GROUPED) {
+    const int first = uniform(tiles[item / nblocks].first);
+    const int count = uniform(tiles[item / nblocks].count);
+    const int i = item - first * nblocks;
+    nb = i / count;
+    tm = first + i % count;
+  } else {
+    const int gsz = kDenseGroupM * nblocks;
+    const int g = item / gsz;
+    const int gm = min(kDenseGroupM, mtiles - g * kDenseGroupM);
+    const int r = item - g * gsz;
+    tm = g * kDenseGroupM + r % gm;
+    nb = r / gm;
+  }
+  return true;
+}
+
+template <class P, bool GROUPED, int BM, int BN, int SCHED>
+__device__ __forceinline__ void lds_gemm_body(const P& p, int mrows, const Tile* tiles,
+                                              const int* ntiles) {
+  constexpr int WM = 2, WN = 4, NW = WM * WN, BK = 64;
+  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+  constexpr int RPI = 8;                      // rows per copy instruction (8 x 128 B)
+  constexpr int NIA = BM / RPI / NW, NIB = BN / RPI / NW, NI = NIA + NIB;
+  static_assert(NIA * RPI * NW == BM && NIB * RPI * NW == BN, "rows per stage");
+  constexpr int ROWB = BK * 2;                // bytes per LDS row
+  constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr bool SEG2 = TwoSegments<P>::value;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  int tm, nb;
+  if (!work_item_uniform<GROUPED>(p.N() / BN, mrows, BM, tiles, ntiles, tm, nb)) return;
+  int e = 0, m0, mcount;
+  if (GROUPED) {
+    e = uniform(tiles[tm].expert);
+    m0 = uniform(tiles[tm].row0);
+    mcount = uniform(tiles[tm].nrows);
+  } else {
+    m0 = tm * BM;
+    mcount = min(BM, mrows - m0);
+  }
+  const int n0 = nb * BN;
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const int wm = w / WN, wn = w % WN;
+  const int nk = p.K() / BK;
+  const int nk0 = SEG2 ? p.K0() / BK : nk;
+
+  // Copy instruction j of wave w fills stage rows RPI (w + NW j) .. + 7; lane
+  // l takes row + l / 8 and the global 16-byte chunk (l % 8) ^ swz with
+  // swz = (row / 2) % 8, which for these rows is (4 (w % 2) + (l / 8) / 2) % 8
+  // for every j: the stage is written already swizzled.
+  const int lr = lane >> 3;
+  const int sw = ((4 * (w & 1)) + (lr >> 1)) & 7;
+  const uint32_t chunk = (uint32_t)(((lane & 7) ^ sw) * 16);
+  // One k segment's copy sources.  A: a per-lane byte offset per instruction
+  // from the tile's first row (strided A) or the array (gathered A); rows
+  // past the tile's count read its first row (never stored).  B: one
+  // per-lane offset (row l / 8 of the instruction, its chunk) from the
+  // tile's first weight row plus a uniform offset per instruction.
+  struct Seg {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    uint32_t ao[NIA];
+    uint32_t bo;
+    int b0, bstep;  // uniform bytes to instruction 0's rows, between instructions
+  };
+  auto make_seg = [&](int seg) __attribute__((always_inline)) {
+    Seg g;
+    const char* pa = GROUPED && P::kGatherA
+                         ? reinterpret_cast<const char*>(seg ? p.a_base1() : p.a_base0())
+                         : reinterpret_cast<const char*>(seg ? p.a_row1(m0) : p.a_row0(m0));
+#pragma unroll
+    for (int j = 0; j < NIA; ++j) {
+      const int row = RPI * (w + NW * j) + lr;
+      const int m = m0 + (row < mcount ? row : 0);
+      g.ao[j] = (uint32_t)(reinterpret_cast<const char*>(seg ? p.a_row1(m) : p.a_row0(m)) - pa) +
+                chunk;
+    }
+    const char* pb = reinterpret_cast<const char*>(seg ? p.b_row1(e, n0) : p.b_row0(e, n0));
+    const int ldb = (int)(seg ? p.ldb1() : p.ldb0()) * 2;
+    g.bo = (uint32_t)(lr * ldb) + chunk;
+    g.b0 = RPI * w * ldb;
+    g.bstep = RPI * NW * ldb;
+    g.ra = buffer_rsrc(pa);
+    g.rb = buffer_rsrc(pb);
+    return g;
+  };
+  // copy one k tile (byte offset kb within the rows) of segment g into stage
+  // buffer buf
+  auto issue = [&](const Seg& g, int kb, int buf) __attribute__((always_inline)) {
+    char* st = smem + buf * STAGE;
+#pragma unroll
+    for (int j = 0; j < NIA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g.ra, (lds_void*)(st + (w + NW * j) * RPI * ROWB),
+                                               16, g.ao[j], kb, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NIB; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          g.rb, (lds_void*)(st + BM * ROWB + (w + NW * j) * RPI * ROWB), 16, g.bo,
+          kb + g.b0 + j * g.bstep, 0, 0);
+  };
+  const Seg seg0 = make_seg(0);
+  auto copy0 = [&](int kt, int buf) { issue(seg0, kt * ROWB, buf); };
+
+  // Fragment reads: lane (r16, kq) of k half ks reads row base + r16, 16-byte
+  // chunk (4 ks + kq) ^ swz(row), and swz(row) = r16 / 2 for these rows.
+  const int r16 = lane & 15, kq = lane >> 4;
+  const uint32_t l0 = r16 * ROWB + (((0 + kq) ^ (r16 >> 1)) << 4);
+  const uint32_t l1 = r16 * ROWB + (((4 + kq) ^ (r16 >> 1)) << 4);
+  const uint32_t aw = (uint32_t)(wm * (BM / WM)) * ROWB;
+  const uint32_t bw = (uint32_t)(BM + wn * (BN / WN)) * ROWB;
+  const bool has_rows = wm * (BM / WM) < mcount;
+
+  f32x4 acc[TN][TM];
+#pragma unroll
+  for (int a = 0; a < TN; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One k step on stage buffer BUF: wait for this wave's copies of the stage,
+  // barrier (everyone's copies landed; everyone is done with the other
+  // buffer), copy the next k tile into the other buffer, then the fragment
+  // reads and MFMAs (k half 0 then 1, the order of tiled_gemm_kernel).
+  // `copy` copies k tile kt + 1 into the other buffer (nullptr: nothing left)
+  auto body = [&](auto buf_c, auto copy, int kt) {
+    constexpr int BUF = decltype(buf_c)::value;
+    constexpr bool COPY = !std::is_same<decltype(copy), std::nullptr_t>::value;
+    wait_vmcnt<0>();
+    stage_barrier_hard();
+    if constexpr (COPY) copy(kt + 1, BUF ^ 1);
+    const char* st = smem + BUF * STAGE;
+    bf16x8 xf[2][TM], wf[2][TN];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t l = ks ? l1 : l0;
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+        xf[ks][t] = *reinterpret_cast<const bf16x8*>(st + aw + l + t * 16 * ROWB);
+#pragma unroll
+      for (int g = 0; g < TN; ++g)
+        wf[ks][g] = *reinterpret_cast<const bf16x8*>(st + bw + l + g * 16 * ROWB);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int g = 0; g < TN; ++g) acc[g][t] = mfma_bf16(wf[ks][g], xf[ks][t], acc[g][t]);
+    if constexpr (SCHED == 1) {
+      // directed order: the first half's fragment reads, the copies spread
+      // over the first MFMAs, the second half's reads under the rest of the
+      // first half's MFMAs, then the second half's MFMAs
+      constexpr int R = TM + TN, M = TM * TN, D = COPY ? NI : 0;
+      constexpr int rest = M - (D < M ? D : M);
+      constexpr int per = rest / R > 0 ? rest / R : 1;
+#pragma unroll
+      for (int i = 0; i < R; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int i = 0; i < D; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, per, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * M, 0);
+    }
+  };
+  // a wave whose token rows all lie past the tile's count only copies
+  auto copy_only = [&](auto buf_c, auto copy, int kt) {
+    constexpr int BUF = decltype(buf_c)::value;
+    wait_vmcnt<0>();
+    stage_barrier_hard();
+    if constexpr (!std::is_same<decltype(copy), std::nullptr_t>::value) copy(kt + 1, BUF ^ 1);
+  };
+
+  // k tiles 2i use buffer 0, 2i + 1 buffer 1; each step copies the next k
+  // tile from its segment and the last step copies nothing.  The k tile
+  // counts of the whole range and of the first segment are even (checked by
+  // the launchers and implied by the tile sizes): an odd tail as a third copy
+  // of the step made the compiler spill the accumulators.
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  // k tiles [k0, k1) of one segment through `copy`; `last_copy` copies the
+  // tile after the segment's last (the next segment's first, or nullptr)
+  auto segment = [&](auto step, int k0, int k1, auto copy, auto last_copy) {
+    int kt = k0;
+    for (; kt + 2 < k1; kt += 2) {
+      step(B0{}, copy, kt);
+      step(B1{}, copy, kt + 1);
+    }
+    step(B0{}, copy, kt);
+    step(B1{}, last_copy, kt + 1);
+  };
+  auto run = [&](auto step) {
+    if constexpr (SEG2) {
+      // segment 0: tiles [0, nk0); segment 1: [nk0, nk)
+      if (nk0 == nk) {
+        segment(step, 0, nk, copy0, nullptr);
+      } else {
+        const Seg seg1 = make_seg(1);
+        auto copy1 = [&](int kt, int buf) { issue(seg1, (kt - nk0) * ROWB, buf); };
+        if (nk0 > 0) segment(step, 0, nk0, copy0, copy1);
+        segment(step, nk0, nk, copy1, nullptr);
+      }
+    } else {
+      segment(step, 0, nk, copy0, nullptr);
+    }
+  };
+  // the first k tile
+  if (!SEG2 || nk0 > 0) {
+    copy0(0, 0);
+  } else {
+    const Seg seg1 = make_seg(1);
+    issue(seg1, 0, 0);
+  }
+  if (!has_rows) {
+    run(copy_only);
+    return;
+  }
+  run(body);
+
+  const int ncol = (lane >> 4) * 4;
+#pragma unroll
+  for (int g = 0; g < TN; ++g)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      const int i = wm * (BM / WM) + t * 16 + r16;
+      if (i < mcount) p.store(e, m0 + i, n0 + wn * (BN / WN) + g * 16 + ncol, acc[g][t]);
+    }
+}
+
+template <class P, bool GROUPED, int BM, int BN, int SCHED>
+__global__ __launch_bounds__(512) void lds_gemm_kernel(P p, int mrows, const Tile* tiles,
+                                                       const int* ntiles) {
+  lds_gemm_body<P, GROUPED, BM, BN, TwoSegments<P>::value ? 0 : SCHED>(p, mrows, tiles, ntiles);
+}
+
 // Grouped expert GEMM with MXFP4 weights for large batches: the main loop of
 // tiled_gemm_kernel (NS = 2 stages of 64 k), with each stage's weight rows
 // decoded from FP4 codes instead of copied.  Every lane owns whole 32-k code
@@ -438,8 +738,12 @@ template <class P, int BM, int BN, int BK, int NS>
 static hipError_t launch_dense(const P& p, int T, hipStream_t s) {
   const long grid = xcd_grid((long)((T + BM - 1) / BM) * (p.N() / BN));
   if (grid <= 0) return hipSuccess;
-  tiled_gemm_kernel<P, false, BM, BN, BK, NS, kWGN><<<grid, 128 * kWGN, 0, s>>>(p, T, nullptr,
-                                                                                nullptr);
+  static_assert(NS == 2 && BK == 64, "dense tiles");
+  if (p.K() % 128 == 0)
+    lds_gemm_kernel<P, false, BM, BN, 1><<<grid, 512, 0, s>>>(p, T, nullptr, nullptr);
+  else
+    tiled_gemm_kernel<P, false, BM, BN, BK, NS, kWGN><<<grid, 128 * kWGN, 0, s>>>(p, T, nullptr,
+                                                                                  nullptr);
   return hipGetLastError();
 }
 
@@ -476,8 +780,17 @@ static hipError_t launch_split(const P& p, int T, float* part, int nsplit, hipSt
   const long gx = xcd_grid((long)((T + BM - 1) / BM) * (p.N() / BN));
   if (gx <= 0) return hipSuccess;
   const SplitK<P> sp{p, p.K() / nsplit, part, T};
-  tiled_gemm_kernel<SplitK<P>, false, BM, BN, kDenseBK, NS, kWGN>
-      <<<dim3(gx, nsplit), 128 * kWGN, 0, s>>>(sp, T, nullptr, nullptr);
+  bool done = false;
+  if constexpr (NS == 2) {
+    if (sp.K() % 128 == 0) {
+      lds_gemm_kernel<SplitK<P>, false, BM, BN, 1>
+          <<<dim3(gx, nsplit), 512, 0, s>>>(sp, T, nullptr, nullptr);
+      done = true;
+    }
+  }
+  if (!done)
+    tiled_gemm_kernel<SplitK<P>, false, BM, BN, kDenseBK, NS, kWGN>
+        <<<dim3(gx, nsplit), 128 * kWGN, 0, s>>>(sp, T, nullptr, nullptr);
   const long n4 = (long)T * p.N() / 4;
   split_reduce_kernel<<<(n4 + 255) / 256, 256, 0, s>>>(p, part, nsplit, T);
   return hipGetLastError();
@@ -519,8 +832,18 @@ static hipError_t launch_expert(const P& p, const Tile* tiles, const int* ntiles
   return launch_grouped<P, kExpBM, 256, kExpBK, 3>(p, tiles, ntiles, max_tiles, s);
 }
 
+// Expert up projection: lds_gemm_kernel when N allows 512-row weight tiles
+// and every gathered latent row lies within the 2 GiB its buffer offsets
+// reach (a row index is below the token count, which is at most the slot
+// count, itself below max_tiles * tile rows).
 hipError_t tiled_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, int max_tiles,
                         hipStream_t s) {
+  if (p.N() % 512 == 0 && p.K() % 128 == 0 && (long)max_tiles * kExpBM * p.K() * 2 < (1L << 31)) {
+    const long grid = xcd_grid((long)max_tiles * (p.N() / 512));
+    if (grid <= 0) return hipSuccess;
+    lds_gemm_kernel<ExpUp, true, kExpBM, 512, 0><<<grid, 512, 0, s>>>(p, 0, tiles, ntiles);
+    return hipGetLastError();
+  }
   return launch_expert(p, tiles, ntiles, max_tiles, s);
 }
 hipError_t tiled_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles, int max_tiles,
