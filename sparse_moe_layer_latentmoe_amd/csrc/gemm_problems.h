@@ -182,6 +182,7 @@ struct ExpUpMx {
   const uint8_t* scales;  // [E, F, R/32]
   uint16_t* h;            // [slots, F]
   int R, F;
+  static constexpr bool kGatherA = true;
   __host__ __device__ int N() const { return F; }
   __host__ __device__ int K() const { return R; }
   __device__ const uint8_t* codes_row(int e, int n) const {
@@ -202,6 +203,7 @@ struct ExpDownMx {
   const uint8_t* scales;  // [E, R, F/32]
   uint16_t* o;            // [slots, R]
   int R, F;
+  static constexpr bool kGatherA = false;
   __host__ __device__ int N() const { return R; }
   __host__ __device__ int K() const { return F; }
   __device__ const uint8_t* codes_row(int e, int n) const {

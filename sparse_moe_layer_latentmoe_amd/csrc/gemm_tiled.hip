@@ -769,7 +769,10 @@ __device__ __forceinline__ void lds_mx_body(const P& p, const Tile* tiles, const
   const int nk = K / BK;
 
   // token copies: instruction j of wave w fills rows 4 (w + NW j) .. + 3,
-  // lane l row + l / 16, LDS slot l % 16 holding chunk (l % 16) ^ (row % 16)
+  // lane l row + l / 16, LDS slot l % 16 holding chunk (l % 16) ^ (row % 16).
+  // Offsets are taken from the tile's first row; they are not negative, as
+  // the dispatch keeps an expert's rows in token order (gathered rows) and
+  // rows read in place follow each other.
   const char* abase = reinterpret_cast<const char*>(p.a_row(m0));
   uint32_t aoff[NIA];
 #pragma unroll
@@ -1050,13 +1053,17 @@ static hipError_t launch_expert_mx(const P& p, const Tile* tiles, const int* nti
 // lds_mx_kernel where its shape conditions hold: N a multiple of 512, K a
 // multiple of 512 (whole groups of four 128-k stages, whose 16 scale bytes
 // per row are then one aligned 16-byte piece), the scales 16-byte aligned,
-// and the gathered latent rows within the 2 GiB its buffer offsets reach
-// (as for tiled_exp_up).
+// and the token rows' byte offsets from the tile's first row within the
+// 2 GiB its buffer offsets reach: gathered rows (up projection) lie less than
+// the token count, itself at most the slot count (below max_tiles * tile
+// rows), rows after it; rows read in place (down projection) lie within the
+// tile's 128.
 template <class P>
 static hipError_t launch_lds_mx(const P& p, const Tile* tiles, const int* ntiles, int max_tiles,
                                 hipStream_t s) {
+  const long a_span = (P::kGatherA ? (long)max_tiles * kExpBM : (long)kExpBM) * p.K() * 2;
   if (p.N() % 512 == 0 && p.K() % 512 == 0 && (reinterpret_cast<uintptr_t>(p.scales) & 15) == 0 &&
-      (long)max_tiles * kExpBM * p.K() * 2 < (1L << 31)) {
+      a_span < (1L << 31)) {
     const long grid = xcd_grid((long)max_tiles * (p.N() / 512));
     if (grid <= 0) return hipSuccess;
     lds_mx_kernel<P, kExpBM, 512><<<grid, 512, 0, s>>>(p, tiles, ntiles);
@@ -1069,11 +1076,9 @@ hipError_t tiled_mx_exp_up(const ExpUpMx& p, const Tile* tiles, const int* ntile
                            hipStream_t s) {
   return launch_lds_mx(p, tiles, ntiles, max_tiles, s);
 }
-// The down projection keeps tiled_mx_kernel: with lds_mx_kernel it measured
-// 5.63-5.77 ms against 5.45 ms on the 8192-token batch.
 hipError_t tiled_mx_exp_down(const ExpDownMx& p, const Tile* tiles, const int* ntiles,
                              int max_tiles, hipStream_t s) {
-  return launch_expert_mx(p, tiles, ntiles, max_tiles, s);
+  return launch_lds_mx(p, tiles, ntiles, max_tiles, s);
 }
 
 }  // namespace lmoe

@@ -24,6 +24,9 @@ MX_SMALL = li.LayerShape(256, 128, 16, 4, 256, 512, 5.0)
 MX_WIDE = li.LayerShape(512, 512, 16, 4, 1024, 512, 5.0)
 # expert width 4096: the down projection's k range is split in two parts
 MX_LONG = li.LayerShape(512, 512, 16, 4, 4096, 512, 5.0)
+# latent 1024 (two groups of four 128-k stages) and expert width 1024: on the
+# tiled path the up projection takes the kernel with the codes staged in LDS
+MX_DEEP = li.LayerShape(512, 1024, 16, 4, 1024, 512, 5.0)
 
 
 @pytest.fixture(scope="module")
@@ -100,6 +103,7 @@ def mx_weights(inp):
     (MX_WIDE, 200, pkg.PATH_AUTO), (MEDIUM, 129, pkg.PATH_AUTO), (MEDIUM, 300, pkg.PATH_AUTO),
     (MEDIUM, 1, pkg.PATH_TILED), (MEDIUM, 64, pkg.PATH_TILED), (MX_WIDE, 200, pkg.PATH_TILED),
     (MX_LONG, 1, pkg.PATH_AUTO), (MX_LONG, 37, pkg.PATH_AUTO),
+    (MX_DEEP, 150, pkg.PATH_TILED), (MX_DEEP, 3, pkg.PATH_TILED),
 ])
 def test_mxfp4_forward_matches_oracle(dev, shape, tokens, path):
     wl = li.Workload("mxfp4", shape, tokens)
