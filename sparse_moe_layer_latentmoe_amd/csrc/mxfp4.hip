@@ -21,15 +21,13 @@
 //             The token fragments are loaded at the same k, so both MFMA
 //             operands agree on which 32 k a step sums over.
 //
-// Streaming the codes at HBM speed is limited by the number of vector-memory
-// instructions, not by bytes or arithmetic: a 16-byte code load carries 32
-// weights, so per code byte the token-fragment and scale loads weigh four
-// times more than in the bf16 kernel.  The main kernel therefore (a) loads
-// both 64-byte halves of every 128-byte code line back to back (the two
-// halves in separate steps let the line leave the cache in between, and the
-// HBM traffic nearly doubles), (b) loads the scales of two 256-k stages with
-// one 16-byte load per row, and (c) splits a work-group's waves over rows,
-// not k, so the token tile is read once per work-group into LDS and shared.
+// A 16-byte code load carries 32 weights, so per code byte the token-fragment
+// and scale loads weigh four times more than in the bf16 kernel, and a
+// lane's codes in the MFMA layout cover only half of each 128-byte line.  The
+// main kernel (stream_mx_lds_kernel) therefore copies the codes into LDS as
+// whole lines with direct, non-temporal loads, copies the token tile into LDS
+// once per work-group, and loads the scales of two 256-k stages with one
+// 16-byte load per row.
 #include <algorithm>
 
 #include "gemm_problems.h"
@@ -187,184 +185,173 @@ __global__ __launch_bounds__(NW * 64) void stream_mx_kernel(P p, const Tile* til
   }
 }
 
-// Grouped expert GEMM for K a multiple of 512 KS (codes and scales 16-byte
-// aligned, N a multiple of (WPG / KS) RG 16).  Work-group = WPG waves on one
-// 16-row token tile: WPG / KS row groups of RG * 16 weight rows, each split
-// over KS waves along k (KS = 1: one wave per row group over the whole k
-// range; KS > 1 shortens the work items, so that the last round of
-// work-groups on the chip is short, and adds the k parts in LDS in a fixed
-// order).  k runs in 256-k stages: per stage a lane loads RG x 2 code blocks
-// (the two halves of each code line together) and reads its 4 x 2 token
-// fragments from LDS; the stage's token tile (16 rows x 256 k for each k
-// part) is copied into LDS by the whole work-group one stage ahead (double
-// buffer, one barrier per stage), and the scales come one 16-byte load per
-// row for a pair of stages, one pair ahead.  Work items (tile, row block) are
-// taken XCD-major.
-template <class P, int RG, int WPG, int KS>
-__global__ __launch_bounds__(WPG * 64) void stream_mx_shared_kernel(P p, const Tile* tiles,
-                                                                    const int* ntiles) {
-  constexpr int XROW = 256 + 8;         // bf16 per LDS token row (16-byte pad: no bank conflicts)
-  constexpr int XT = 16 * XROW;         // one k part's token tile
-  constexpr int XP = KS * 512 / (WPG * 64);  // 16-byte token pieces per thread per stage
-  constexpr int NRG = WPG / KS;         // row groups per work-group
-  static_assert(XP >= 1 && XP * WPG * 64 == KS * 512 && NRG * KS == WPG, "WPG, KS");
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][KS * XT];
+namespace {
 
-  // Consecutive blocks go to the 8 XCDs in turn; block b runs work item
-  // (b % 8) * (n / 8) + b / 8 so that the items of one tile (consecutive)
-  // share an XCD and its L2.  Only the live tiles' items are numbered.
-  const int nwg = p.N() / (NRG * 16 * RG);
-  const int nwork = *ntiles * nwg;
+typedef __attribute__((address_space(3))) void lds_dst_t;
+
+// s_waitcnt with only the vector-memory counter set to N (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt and lgkmcnt left at their maximum).
+template <int N>
+__device__ __forceinline__ void vmem_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// raw buffer over 2 GiB from `base` (the hardware returns 0 past it)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFF0,
+                                           0x00020000);
+}
+
+}  // namespace
+
+// Grouped expert GEMM for K a multiple of 512 and N of 256 (codes and scales
+// 16-byte aligned).  Work-group = 8 waves on one 16-row token tile and 256
+// weight rows, each wave 2 row groups (32 rows) over the whole k range, in
+// stages of 256 k.  Everything a stage needs from memory arrives by direct
+// global -> LDS loads issued one stage ahead:
+//  - each wave copies its own 32 rows' codes of the stage (32 x 128 bytes,
+//    four loads of 8 whole lines) with the non-temporal hint into its own two
+//    LDS slots.  Measured on the decode batch's up-projection codes with no
+//    arithmetic: 7.1 TB/s, the read ceiling of the chip, against 6.2-6.3 TB/s
+//    for these bytes loaded into registers 16 rows x 64 bytes at a time (the
+//    MFMA layout, both halves of a line back to back) and 6.2-6.3 without the
+//    hint;
+//  - the stage's token tile (16 rows x 512 bytes) is copied by the whole
+//    work-group, one load per wave;
+//  - the scale bytes of a pair of stages come in one 16-byte register load per
+//    row, one pair ahead.
+// One barrier per stage.  LDS rows are XOR-swizzled: code row r keeps its
+// 16-byte chunk c at c ^ (r % 8), token row t its chunk c at c ^ t.  Work
+// items (tile, row block) are taken XCD-major.  The products and their order
+// are those of the general kernel's k assignment: lane (r, q) of step u in
+// half h of a stage takes code bytes 4u..4u+3 of block 4h + q of row r.
+template <class P>
+__device__ __forceinline__ void stream_mx_lds_body(const P& p, const Tile* tiles,
+                                                   const int* ntiles) {
+  constexpr int NW = 8, RG = 2, ROWS = NW * 16 * RG;
+  constexpr int CSLOT = 16 * RG * 128;  // one wave's codes of one stage
+  constexpr int TSLOT = 16 * 512;       // the token tile of one stage
+  __shared__ __attribute__((aligned(1024))) char smem[NW * 2 * CSLOT + 2 * TSLOT];
+
+  const int nwg = p.N() / ROWS;
+  const int nwork = __builtin_amdgcn_readfirstlane(*ntiles) * nwg;
   const int b = blockIdx.x;
   if (b >= nwork) return;
   const int per = nwork >> 3;
   const int item = b < (per << 3) ? (b & 7) * per + (b >> 3) : b;
   const int nb = item % nwg;
-  const Tile t = tiles[item / nwg];
-  const int e = t.expert, m0 = t.row0, mcount = t.nrows;
-
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tix = item / nwg;
+  const int e = __builtin_amdgcn_readfirstlane(tiles[tix].expert);
+  const int m0 = __builtin_amdgcn_readfirstlane(tiles[tix].row0);
+  const int mcount = __builtin_amdgcn_readfirstlane(tiles[tix].nrows);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, q = lane >> 4;
-  const int rgw = w / KS, kh = w % KS;  // this wave's row group and k part
-  const int klen = p.K() / KS;
-  const int nst = klen / 256;           // stages per k part (even)
-  const int n0 = (nb * NRG + rgw) * (16 * RG);
+  const int nst = p.K() / 256;
+  const int kb = p.K() / 2;  // code bytes per row
+  const int n0 = nb * ROWS + w * 16 * RG;
 
-  const uint8_t* cw[RG];
+  // code loads: load j fills this wave's rows 8j .. 8j + 7, lane l row
+  // 8j + l / 8, LDS position l % 8 holding chunk (l % 8) ^ (row % 8)
+  const char* cbase = reinterpret_cast<const char*>(p.codes_row(e, n0));
+  const __amdgpu_buffer_rsrc_t rc = raw_buffer(cbase);
+  const uint32_t coff = (uint32_t)((lane >> 3) * kb + (((lane & 7) ^ ((lane >> 3) & 7)) << 4));
+  char* const cslots = smem + w * 2 * CSLOT;
+  // token load: wave w fills token rows 2w and 2w + 1, lane l row 2w + l / 32,
+  // LDS position l % 32 holding chunk (l % 32) ^ row; rows past the tile's
+  // count read its first row (never stored).  Offsets from the tile's first
+  // row are not negative: the dispatch keeps an expert's rows in token order.
+  const char* abase = reinterpret_cast<const char*>(p.a_row(m0));
+  const int trow = 2 * w + (lane >> 5);
+  const char* tsrc = reinterpret_cast<const char*>(p.a_row(m0 + (trow < mcount ? trow : 0)));
+  const uint32_t toff = (uint32_t)(tsrc - abase) + (uint32_t)(((lane & 31) ^ trow) << 4);
+  const __amdgpu_buffer_rsrc_t ra = raw_buffer(abase);
+  char* const tslots = smem + NW * 2 * CSLOT;
+  auto issue = [&](int st) __attribute__((always_inline)) {
+    char* cs = cslots + (st & 1) * CSLOT;
+#pragma unroll
+    for (int j = 0; j < 2 * RG; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_dst_t*)(cs + j * 1024), 16, coff,
+                                               st * 128 + j * 8 * kb, 0, 2 /* nt */);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_dst_t*)(tslots + (st & 1) * TSLOT + w * 1024),
+                                             16, toff, st * 512, 0, 0);
+  };
   const uint8_t* sw[RG];
 #pragma unroll
-  for (int g = 0; g < RG; ++g) {
-    const int row = n0 + g * 16 + r16;
-    cw[g] = p.codes_row(e, row) + kh * (klen / 2) + q * 16;
-    sw[g] = p.scales_row(e, row) + kh * (klen / 32);
-  }
-  // token rows past the tile's count copy the tile's first row (not stored)
-  const uint16_t* xsrc[XP];
-  int xdst[XP];
+  for (int g = 0; g < RG; ++g) sw[g] = p.scales_row(e, n0 + g * 16 + r16);
+  u32x4 scur[RG], snext[RG];
 #pragma unroll
-  for (int j = 0; j < XP; ++j) {
-    const int gp = j * WPG * 64 + threadIdx.x;
-    const int part = gp / 512, piece = gp % 512;
-    const int row = piece >> 5, col = (piece & 31) * 8;
-    xsrc[j] = p.a_row(m0 + (row < mcount ? row : 0)) + part * klen + col;
-    xdst[j] = part * XT + row * XROW + col;
-  }
-  const int xrd = kh * XT + r16 * XROW + q * 32;
-
+  for (int g = 0; g < RG; ++g) snext[g] = *reinterpret_cast<const u32x4*>(sw[g]);
   f32x4 acc[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 CA[2][RG], CB[2][RG];  // code blocks of two stages, [half][row group]
-  u32x4 S0[RG], S1[RG];        // scale bytes of the current and the next stage pair
-  bf16x8 XG[XP];               // token pieces on their way to LDS
-  auto load_codes = [&](u32x4(&C)[2][RG], int st) {
+  issue(0);
+  for (int st = 0; st < nst; ++st) {
+    // this stage's loads (every wave's) have landed, and every wave is done
+    // with the slots the next stage's loads overwrite
+    vmem_wait<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (st + 1 < nst) issue(st + 1);
+    if ((st & 1) == 0) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int g = 0; g < RG; ++g) scur[g] = snext[g];
+      if (st + 2 < nst) {
 #pragma unroll
-      for (int g = 0; g < RG; ++g)
-        C[h][g] = *reinterpret_cast<const u32x4*>(cw[g] + st * 128 + h * 64);
-  };
-  auto load_scales = [&](u32x4(&S)[RG], int st) {
+        for (int g = 0; g < RG; ++g)
+          snext[g] = *reinterpret_cast<const u32x4*>(sw[g] + (st + 2) * 8);
+      }
+    }
+    const char* cs = cslots + (st & 1) * CSLOT;
+    const char* ts = tslots + (st & 1) * TSLOT;
 #pragma unroll
-    for (int g = 0; g < RG; ++g) S[g] = *reinterpret_cast<const u32x4*>(sw[g] + st * 8);
-  };
-  auto load_tokens = [&](int st) {
-#pragma unroll
-    for (int j = 0; j < XP; ++j) XG[j] = load8(xsrc[j] + st * 256);
-  };
-  auto store_tokens = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < XP; ++j) *reinterpret_cast<bf16x8*>(&xs[buf][xdst[j]]) = XG[j];
-  };
-  // one stage: scale byte q of dword 2*odd + h is the scale of this lane's
-  // block in half h of the stage
-  auto compute = [&](const u32x4(&C)[2][RG], int buf, int odd) {
-    bf16x8 X[2][4];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 x[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        X[h][u] = *reinterpret_cast<const bf16x8*>(&xs[buf][xrd + h * 128 + u * 8]);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
+        x[u] = *reinterpret_cast<const bf16x8*>(ts + r16 * 512 + (((h * 16 + q * 4 + u) ^ r16) << 4));
 #pragma unroll
       for (int g = 0; g < RG; ++g) {
-        const float sc = mx_scale(__builtin_amdgcn_ubfe(S0[g][odd * 2 + h], q * 8, 8));
+        const int row = g * 16 + r16;
+        const u32x4 c = *reinterpret_cast<const u32x4*>(cs + row * 128 + (((h * 4 + q) ^ (row & 7)) << 4));
+        const float sc = mx_scale(__builtin_amdgcn_ubfe(scur[g][(st & 1) * 2 + h], q * 8, 8));
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[g] = mfma_bf16(mx_decode8(C[h][g][u], sc), X[h][u], acc[g]);
+        for (int u = 0; u < 4; ++u) acc[g] = mfma_bf16(mx_decode8(c[u], sc), x[u], acc[g]);
       }
-  };
-
-  load_tokens(0);
-  load_codes(CA, 0);
-  load_scales(S0, 0);
-  store_tokens(0);
-  load_tokens(1);
-  __syncthreads();
-  for (int st = 0; st < nst; st += 2) {
-    const bool more = st + 2 < nst;
-    load_codes(CB, st + 1);
-    if (more) load_scales(S1, st + 2);
-    compute(CA, 0, 0);
-    store_tokens(1);
-    if (more) load_tokens(st + 2);
-    __syncthreads();
-    if (more) load_codes(CA, st + 2);
-    compute(CB, 1, 1);
-    if (more) {
-      store_tokens(0);
-      load_tokens(st + 3);
-#pragma unroll
-      for (int g = 0; g < RG; ++g) S0[g] = S1[g];
     }
-    __syncthreads();
   }
-
   const int ncol = q * 4;
-  if constexpr (KS == 1) {
 #pragma unroll
-    for (int g = 0; g < RG; ++g)
-      if (r16 < mcount) p.store(e, m0 + r16, n0 + g * 16 + ncol, acc[g]);
-  } else {
-    // k parts added in part order (deterministic)
-    __shared__ f32x4 red[KS][NRG][RG][64];
-#pragma unroll
-    for (int g = 0; g < RG; ++g) red[kh][rgw][g][lane] = acc[g];
-    __syncthreads();
-    if (kh == 0) {
-#pragma unroll
-      for (int g = 0; g < RG; ++g) {
-        f32x4 sm = red[0][rgw][g][lane];
-#pragma unroll
-        for (int v = 1; v < KS; ++v) sm += red[v][rgw][g][lane];
-        if (r16 < mcount) p.store(e, m0 + r16, n0 + g * 16 + ncol, sm);
-      }
-    }
-  }
+  for (int g = 0; g < RG; ++g)
+    if (r16 < mcount) p.store(e, m0 + r16, n0 + g * 16 + ncol, acc[g]);
 }
 
-// The shared-token kernel where its conditions hold; otherwise the general
-// kernel with the largest of 4, 2, 1 waves per work-group whose k share is a
-// whole number of 128-k steps (K is a multiple of 128).
+template <class P>
+__global__ __launch_bounds__(512) void stream_mx_lds_kernel(P p, const Tile* tiles,
+                                                            const int* ntiles) {
+  stream_mx_lds_body<P>(p, tiles, ntiles);
+}
+
+// stream_mx_lds_kernel where its conditions hold (K a multiple of 512, N of
+// 256, codes and scales 16-byte aligned, and the token rows' byte offsets
+// from a tile's first row within the 2 GiB of a buffer descriptor: gathered
+// rows lie less than the token count, at most the slot count, itself at most
+// max_tiles * 16, rows after it; rows read in place lie within the tile's 16);
+// otherwise the general kernel with the largest of 4, 2, 1 waves per
+// work-group whose k share is a whole number of 128-k steps (K is a multiple
+// of 128).
 template <class P>
 static hipError_t launch_mx(const P& p, const Tile* tiles, const int* ntiles, int max_tiles,
                             hipStream_t s) {
-  constexpr int kSharedRG = 2, kSharedWPG = 8;
   const bool aligned = ((reinterpret_cast<uintptr_t>(p.codes) | reinterpret_cast<uintptr_t>(p.scales)) & 15) == 0;
-  if (p.K() % 512 == 0 && p.N() % (kSharedWPG * 16 * kSharedRG) == 0 && aligned) {
-    // long k ranges (the down projection, k = 5120) in two parts: measured at
-    // the decode batch 0.403 vs 0.435 ms (the work-groups' last round on the
-    // chip is shorter); the up projection (k = 2048) is not faster that way
-    if (p.K() >= 4096 && p.K() % 1024 == 0) {
-      const long grid = (long)max_tiles * (p.N() / (kSharedWPG / 2 * 16 * kSharedRG));
-      if (grid <= 0) return hipSuccess;
-      stream_mx_shared_kernel<P, kSharedRG, kSharedWPG, 2><<<grid, kSharedWPG * 64, 0, s>>>(p, tiles, ntiles);
-      return hipGetLastError();
-    }
-    const long grid = (long)max_tiles * (p.N() / (kSharedWPG * 16 * kSharedRG));
+  const long a_span = (P::kGatherA ? (long)max_tiles * 16 : 16L) * p.K() * 2;
+  if (p.K() % 512 == 0 && p.N() % 256 == 0 && aligned && a_span < (1L << 31)) {
+    const long grid = (long)max_tiles * (p.N() / 256);
     if (grid <= 0) return hipSuccess;
-    stream_mx_shared_kernel<P, kSharedRG, kSharedWPG, 1><<<grid, kSharedWPG * 64, 0, s>>>(p, tiles, ntiles);
+    stream_mx_lds_kernel<P><<<grid, 512, 0, s>>>(p, tiles, ntiles);
     return hipGetLastError();
   }
   constexpr int RG = 4;
