@@ -19,10 +19,11 @@ from oracle import lmoe_oracle as O
 pytestmark = pytest.mark.gpu
 
 MX_SMALL = li.LayerShape(256, 128, 16, 4, 256, 512, 5.0)
-# latent and expert widths multiples of 512: both expert GEMMs take the
-# shared-token kernel (MX_SMALL takes the general one, MEDIUM one of each)
+# latent and expert widths multiples of 512: both streaming expert GEMMs take
+# the kernel with the codes copied into LDS (MX_SMALL takes the general one,
+# MEDIUM one of each)
 MX_WIDE = li.LayerShape(512, 512, 16, 4, 1024, 512, 5.0)
-# expert width 4096: the down projection's k range is split in two parts
+# expert width 4096: a long k range (16 stages) for the down projection
 MX_LONG = li.LayerShape(512, 512, 16, 4, 4096, 512, 5.0)
 # latent 1024 (two groups of four 128-k stages) and expert width 1024: on the
 # tiled path the up projection takes the kernel with the codes staged in LDS
