@@ -54,6 +54,34 @@ def test_noalloc_matches_the_handle_forward(dev, shape, tokens, path):
     layer.close()
 
 
+# latent and expert widths multiples of 512: the MXFP4 streaming kernel that
+# copies the codes into LDS; MEDIUM at 200 tokens: the LDS-tiled MXFP4 GEMMs
+MX_WIDE = li.LayerShape(512, 512, 16, 4, 1024, 512, 5.0)
+
+
+@pytest.mark.parametrize("shape,tokens", [(MX_WIDE, (64, 13)), (MEDIUM, (200, 70))])
+def test_noalloc_matches_the_handle_forward_mxfp4(dev, shape, tokens):
+    T0 = tokens[0]
+    say(f"[noalloc mxfp4 D={shape.hidden_size} E={shape.n_routed_experts} T={tokens}]")
+    wl = li.Workload("noalloc", shape, T0)
+    inp = li.make_inputs(wl, dev)
+    w = weight_dict(inp)
+    up_c, up_s = pkg.quantize_mxfp4(inp.expert_up)
+    dn_c, dn_s = pkg.quantize_mxfp4(inp.expert_down)
+    w.update(expert_up=None, expert_down=None, expert_up_mxfp4=up_c, expert_up_scale=up_s,
+             expert_down_mxfp4=dn_c, expert_down_scale=dn_s)
+    layer = pkg.LatentMoE(shape, w, T0, expert_format=pkg.EXPERTS_MXFP4)
+    for T in tokens:
+        x = inp.x[:T].contiguous() if T < T0 else inp.x
+        want = layer.forward(x)
+        got = torch.full_like(x, float("nan"))
+        layer.forward_noalloc_into(x, got)
+        torch.cuda.synchronize()
+        say(f"  T={T}: equal {torch.equal(got, want)}")
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), T
+    layer.close()
+
+
 def test_noalloc_refuses_forwards_beyond_its_scratch(dev):
     """A full-shape forward of 192 tokens needs ~130 MB of scratch: refused
     with LMOE_ERR_SCRATCH, nothing launched (y keeps its contents)."""
