@@ -266,17 +266,21 @@ hipError_t stream_proj_in(const ProjIn& p, hipStream_t s) {
 hipError_t stream_proj_out(const ProjOut& p, hipStream_t s) {
   return launch_dense(p, Shape{8, 2, 1}, p.T, s);
 }
-// Expert GEMMs, measured on the decode (T = 32, ~380 experts touched) and
-// speculative-verify (T = 192, all 512) problems: up projection 8 waves x 2
-// row groups (1117 / 1575 us against 1151 / 1618 us for 4 x 4), down
-// projection 4 x 4 (the best at T = 192, within 1% of the best at T = 32).
+// Expert GEMMs, measured on the decode (T = 32, ~380 experts touched, 1.4
+// rows each on average) and speculative-verify (T = 192, all 512, 8.3 rows)
+// problems: up projection 8 waves x 2 row groups (1117 / 1575 us against
+// 1151 / 1618 us for 4 x 4); down projection 8 waves x 1 row group x 2 k
+// chunks per stage where experts average at most 2 rows (1113 against 1140 us
+// for 4 x 4 at T = 32), else 4 x 4 (1584 us at T = 192, against 1632 for
+// 8 x 2 and 1732 for 8 x 1 x 2).
 hipError_t stream_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, int max_tiles,
                          hipStream_t s) {
   return launch_grouped(p, Shape{8, 2, 1}, tiles, ntiles, max_tiles, s);
 }
 hipError_t stream_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles, int max_tiles,
-                           hipStream_t s) {
-  return launch_grouped(p, Shape{4, 4, 1}, tiles, ntiles, max_tiles, s);
+                           int rows_per_expert, hipStream_t s) {
+  return launch_grouped(p, rows_per_expert <= 2 ? Shape{8, 1, 2} : Shape{4, 4, 1}, tiles, ntiles,
+                        max_tiles, s);
 }
 
 }  // namespace lmoe

@@ -19,8 +19,10 @@ hipError_t stream_proj_in(const ProjIn& p, hipStream_t s);
 hipError_t stream_proj_out(const ProjOut& p, hipStream_t s);
 hipError_t stream_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, int max_tiles,
                          hipStream_t s);
+// rows_per_expert: the batch's average rows per expert, ceil(T K / E) (it
+// picks the launch shape)
 hipError_t stream_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles, int max_tiles,
-                           hipStream_t s);
+                           int rows_per_expert, hipStream_t s);
 constexpr int kStreamTileM = 16;
 // Dense GEMMs stream weights for batches of at most this many tokens.
 constexpr int kStreamDenseMaxTokens = 64;

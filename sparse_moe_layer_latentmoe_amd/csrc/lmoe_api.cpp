@@ -374,7 +374,8 @@ lmoe_status run_forward(const lmoe_config& c, const lmoe_weights& w, const Layou
   } else {
     ExpDown pdn{H, w.expert_down, O, R, F};
     if (!ok(expert_tiled ? tiled_exp_down(pdn, tiles, ntiles, ntile_max, s)
-                         : stream_exp_down(pdn, tiles, ntiles, ntile_max, s)))
+                         : stream_exp_down(pdn, tiles, ntiles, ntile_max,
+                                           static_cast<int>((T * K + E - 1) / E), s)))
       return LMOE_ERR_HIP;
   }
   if (!done("expert_down") || !mark()) return LMOE_ERR_HIP;
