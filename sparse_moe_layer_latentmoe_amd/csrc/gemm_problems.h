@@ -141,6 +141,10 @@ struct ExpUp {
   __device__ void store(int, int p, int n, f32x4 v) const {
     store4_bf16_relu_sq(h + (size_t)p * F + n, v);
   }
+  // non-temporal: for the weight-streaming kernel (few rows per expert)
+  __device__ void store_nt(int, int p, int n, f32x4 v) const {
+    store4_bf16_relu_sq_nt(h + (size_t)p * F + n, v);
+  }
 };
 
 // Expert down projection (Step 6): O[p] = H[p] Wdn[e]^T, stored bf16; the
@@ -168,6 +172,9 @@ struct ExpDown {
   __device__ const uint16_t* a_row1(int) const { return nullptr; }
   __device__ void store(int, int p, int n, f32x4 v) const {
     store4_bf16(o + (size_t)p * R + n, v);
+  }
+  __device__ void store_nt(int, int p, int n, f32x4 v) const {
+    store4_bf16_nt(o + (size_t)p * R + n, v);
   }
 };
 

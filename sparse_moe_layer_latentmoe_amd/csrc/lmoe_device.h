@@ -64,6 +64,16 @@ __device__ __forceinline__ void store4_bf16(uint16_t* p, f32x4 v) {
   *reinterpret_cast<u16x4*>(p) = o;
 }
 
+// The same with the non-temporal hint.
+__device__ __forceinline__ void store4_bf16_nt(uint16_t* p, f32x4 v) {
+  u16x4 o;
+  o[0] = f32_to_bf16(v[0]);
+  o[1] = f32_to_bf16(v[1]);
+  o[2] = f32_to_bf16(v[2]);
+  o[3] = f32_to_bf16(v[3]);
+  __builtin_nontemporal_store(o, reinterpret_cast<u16x4*>(p));
+}
+
 __device__ __forceinline__ void store4_bf16_relu_sq(uint16_t* p, f32x4 v) {
   f32x4 a;
   a[0] = relu_sq(v[0]);
@@ -71,6 +81,15 @@ __device__ __forceinline__ void store4_bf16_relu_sq(uint16_t* p, f32x4 v) {
   a[2] = relu_sq(v[2]);
   a[3] = relu_sq(v[3]);
   store4_bf16(p, a);
+}
+
+__device__ __forceinline__ void store4_bf16_relu_sq_nt(uint16_t* p, f32x4 v) {
+  f32x4 a;
+  a[0] = relu_sq(v[0]);
+  a[1] = relu_sq(v[1]);
+  a[2] = relu_sq(v[2]);
+  a[3] = relu_sq(v[3]);
+  store4_bf16_nt(p, a);
 }
 
 // Work tile of the grouped expert GEMMs: rows [row0, row0 + nrows) of the
