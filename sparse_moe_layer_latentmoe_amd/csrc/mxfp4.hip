@@ -205,10 +205,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base) {
 
 }  // namespace
 
-// Grouped expert GEMM for K a multiple of 512 and N of 256 (codes and scales
-// 16-byte aligned).  Work-group = 8 waves on one 16-row token tile and 256
+// Grouped expert GEMM for K a multiple of 512 and N of 128 (codes and scales
+// 16-byte aligned).  Work-group = 4 waves on one 16-row token tile and 128
 // weight rows, each wave 2 row groups (32 rows) over the whole k range, in
-// stages of 256 k.  Everything a stage needs from memory arrives by direct
+// stages of 256 k (8 waves on 256 rows measured 1-2% slower: 332 vs 324 us
+// for the decode batch's down projection).  Everything a stage needs from memory arrives by direct
 // global -> LDS loads issued one stage ahead:
 //  - each wave copies its own 32 rows' codes of the stage (32 x 128 bytes,
 //    four loads of 8 whole lines) with the non-temporal hint into its own two
@@ -218,7 +219,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base) {
 //    MFMA layout, both halves of a line back to back) and 6.2-6.3 without the
 //    hint;
 //  - the stage's token tile (16 rows x 512 bytes) is copied by the whole
-//    work-group, one load per wave;
+//    work-group, two loads per wave;
 //  - the scale bytes of a pair of stages come in one 16-byte register load per
 //    row, one pair ahead.
 // One barrier per stage.  LDS rows are XOR-swizzled: code row r keeps its
@@ -226,12 +227,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base) {
 // items (tile, row block) are taken XCD-major.  The products and their order
 // are those of the general kernel's k assignment: lane (r, q) of step u in
 // half h of a stage takes code bytes 4u..4u+3 of block 4h + q of row r.
+// 48 KB of LDS per work-group, three work-groups per CU.
 template <class P>
 __device__ __forceinline__ void stream_mx_lds_body(const P& p, const Tile* tiles,
                                                    const int* ntiles) {
-  constexpr int NW = 8, RG = 2, ROWS = NW * 16 * RG;
+  constexpr int NW = 4, RG = 2, ROWS = NW * 16 * RG;
   constexpr int CSLOT = 16 * RG * 128;  // one wave's codes of one stage
   constexpr int TSLOT = 16 * 512;       // the token tile of one stage
+  constexpr int TPW = 8 / NW;           // token loads (2 rows each) per wave
   __shared__ __attribute__((aligned(1024))) char smem[NW * 2 * CSLOT + 2 * TSLOT];
 
   const int nwg = p.N() / ROWS;
@@ -258,14 +261,19 @@ __device__ __forceinline__ void stream_mx_lds_body(const P& p, const Tile* tiles
   const __amdgpu_buffer_rsrc_t rc = raw_buffer(cbase);
   const uint32_t coff = (uint32_t)((lane >> 3) * kb + (((lane & 7) ^ ((lane >> 3) & 7)) << 4));
   char* const cslots = smem + w * 2 * CSLOT;
-  // token load: wave w fills token rows 2w and 2w + 1, lane l row 2w + l / 32,
-  // LDS position l % 32 holding chunk (l % 32) ^ row; rows past the tile's
-  // count read its first row (never stored).  Offsets from the tile's first
-  // row are not negative: the dispatch keeps an expert's rows in token order.
+  // token loads: load i of wave w fills token rows 2v and 2v + 1 (v = TPW w +
+  // i), lane l row 2v + l / 32, LDS position l % 32 holding chunk (l % 32) ^
+  // row; rows past the tile's count read its first row (never stored).
+  // Offsets from the tile's first row are not negative: the dispatch keeps an
+  // expert's rows in token order.
   const char* abase = reinterpret_cast<const char*>(p.a_row(m0));
-  const int trow = 2 * w + (lane >> 5);
-  const char* tsrc = reinterpret_cast<const char*>(p.a_row(m0 + (trow < mcount ? trow : 0)));
-  const uint32_t toff = (uint32_t)(tsrc - abase) + (uint32_t)(((lane & 31) ^ trow) << 4);
+  uint32_t toff[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int trow = 2 * (TPW * w + i) + (lane >> 5);
+    const char* tsrc = reinterpret_cast<const char*>(p.a_row(m0 + (trow < mcount ? trow : 0)));
+    toff[i] = (uint32_t)(tsrc - abase) + (uint32_t)(((lane & 31) ^ trow) << 4);
+  }
   const __amdgpu_buffer_rsrc_t ra = raw_buffer(abase);
   char* const tslots = smem + NW * 2 * CSLOT;
   auto issue = [&](int st) __attribute__((always_inline)) {
@@ -274,8 +282,11 @@ __device__ __forceinline__ void stream_mx_lds_body(const P& p, const Tile* tiles
     for (int j = 0; j < 2 * RG; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rc, (lds_dst_t*)(cs + j * 1024), 16, coff,
                                                st * 128 + j * 8 * kb, 0, 2 /* nt */);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_dst_t*)(tslots + (st & 1) * TSLOT + w * 1024),
-                                             16, toff, st * 512, 0, 0);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (lds_dst_t*)(tslots + (st & 1) * TSLOT + (TPW * w + i) * 1024), 16, toff[i],
+          st * 512, 0, 0);
   };
   const uint8_t* sw[RG];
 #pragma unroll
@@ -330,13 +341,13 @@ __device__ __forceinline__ void stream_mx_lds_body(const P& p, const Tile* tiles
 }
 
 template <class P>
-__global__ __launch_bounds__(512) void stream_mx_lds_kernel(P p, const Tile* tiles,
+__global__ __launch_bounds__(256) void stream_mx_lds_kernel(P p, const Tile* tiles,
                                                             const int* ntiles) {
   stream_mx_lds_body<P>(p, tiles, ntiles);
 }
 
 // stream_mx_lds_kernel where its conditions hold (K a multiple of 512, N of
-// 256, codes and scales 16-byte aligned, and the token rows' byte offsets
+// 128, codes and scales 16-byte aligned, and the token rows' byte offsets
 // from a tile's first row within the 2 GiB of a buffer descriptor: gathered
 // rows lie less than the token count, at most the slot count, itself at most
 // max_tiles * 16, rows after it; rows read in place lie within the tile's 16);
@@ -348,10 +359,10 @@ static hipError_t launch_mx(const P& p, const Tile* tiles, const int* ntiles, in
                             hipStream_t s) {
   const bool aligned = ((reinterpret_cast<uintptr_t>(p.codes) | reinterpret_cast<uintptr_t>(p.scales)) & 15) == 0;
   const long a_span = (P::kGatherA ? (long)max_tiles * 16 : 16L) * p.K() * 2;
-  if (p.K() % 512 == 0 && p.N() % 256 == 0 && aligned && a_span < (1L << 31)) {
-    const long grid = (long)max_tiles * (p.N() / 256);
+  if (p.K() % 512 == 0 && p.N() % 128 == 0 && aligned && a_span < (1L << 31)) {
+    const long grid = (long)max_tiles * (p.N() / 128);
     if (grid <= 0) return hipSuccess;
-    stream_mx_lds_kernel<P><<<grid, 512, 0, s>>>(p, tiles, ntiles);
+    stream_mx_lds_kernel<P><<<grid, 256, 0, s>>>(p, tiles, ntiles);
     return hipGetLastError();
   }
   constexpr int RG = 4;
