@@ -13,10 +13,11 @@
 //             element |w| / X rounded to the nearest E2M1 magnitude with
 //             ties to the even code (zero mantissa bit), clamped at 6,
 //             signed unless it rounds to 0.
-//   stream    like the bf16 weight-streaming GEMM, with one lane loading the
-//             16 code bytes of one block (32 k of one row): the four lanes of
-//             a row cover 128 consecutive k, and MFMA step u takes code bytes
-//             4u..4u+3 of every lane, converted with
+//   stream    like the bf16 weight-streaming GEMM, with one lane taking the
+//             16 code bytes of one block (32 k of one row; from LDS in the
+//             main kernel, from global memory in the general one): the four
+//             lanes of a row cover 128 consecutive k, and MFMA step u takes
+//             code bytes 4u..4u+3 of every lane, converted with
 //             v_cvt_scalef32_pk_bf16_fp4 (element 0 = low nibble, measured).
 //             The token fragments are loaded at the same k, so both MFMA
 //             operands agree on which 32 k a step sums over.
