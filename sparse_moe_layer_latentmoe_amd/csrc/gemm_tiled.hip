@@ -1,5 +1,7 @@
 // LDS-tiled bf16 MFMA GEMM for large token counts (prefill-sized batches),
-// where the layer is bound by matrix-core throughput.
+// where the layer is bound by matrix-core throughput, and its MXFP4 forms
+// (expert weights as FP4 codes decoded before the MFMAs: lds_mx_kernel, and
+// tiled_mx_kernel for the shapes that one does not take).
 //
 // Work-group tile: BM token rows x BN weight rows, k in steps of BK.  Eight
 // waves (2 along tokens x 4 along weights) each own a (BM/2) x (BN/4)
