@@ -731,9 +731,11 @@ __global__ __launch_bounds__(128 * WGN) void tiled_mx_kernel(P p, const Tile* ti
 // and decoded to bf16 in registers right before the MFMAs, so the copy
 // stream into LDS per flop is 2.4x smaller than with bf16 weights (the
 // stream that bounds the bf16 expert GEMMs).  Tile: 128 token rows x 512
-// weight rows, eight waves (2 x 4, 64 x 128 accumulators each), k in stages
-// of 128, two stages in LDS (2 x 64 KB) plus the scale bytes of two groups of
-// four stages (2 x 8 KB), everything copied with 16-byte direct loads.
+// weight rows, eight waves in WM x (8 / WM) (WM = 2: 64 x 128 accumulators
+// each; WM = 1: 128 x 64, each decoded weight fragment then feeding eight
+// MFMAs instead of four), k in stages of 128, two stages in LDS (2 x 64 KB)
+// plus the scale bytes of two groups of four stages (2 x 8 KB), everything
+// copied with 16-byte direct loads.
 //
 // k assignment inside a stage: MFMA lane (r, q) (q = lane / 16) covers the
 // 32 consecutive k of block q of the stage (one scale byte) and step s of
@@ -745,9 +747,9 @@ __global__ __launch_bounds__(128 * WGN) void tiled_mx_kernel(P p, const Tile* ti
 //
 // LDS rows are XOR-swizzled: token row t (256 bytes) keeps its 16-byte chunk
 // c at c ^ (t % 16); code row n (64 bytes) its chunk q at q ^ ((n / 4) % 4).
-template <class P, int BM, int BN>
+template <class P, int BM, int BN, int WM = 2>
 __device__ __forceinline__ void lds_mx_body(const P& p, const Tile* tiles, const int* ntiles) {
-  constexpr int WM = 2, WN = 4, NW = WM * WN, BK = 128;
+  constexpr int WN = 8 / WM, NW = WM * WN, BK = 128;
   constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
   constexpr int AROW = BK * 2, CROW = BK / 2;   // bytes per token row, per code row
   constexpr int AST = BM * AROW, CST = BN * CROW;
@@ -907,9 +909,9 @@ __device__ __forceinline__ void lds_mx_body(const P& p, const Tile* tiles, const
     }
 }
 
-template <class P, int BM, int BN>
+template <class P, int BM, int BN, int WM = 2>
 __global__ __launch_bounds__(512) void lds_mx_kernel(P p, const Tile* tiles, const int* ntiles) {
-  lds_mx_body<P, BM, BN>(p, tiles, ntiles);
+  lds_mx_body<P, BM, BN, WM>(p, tiles, ntiles);
 }
 
 // Tile shapes used per problem (token rows x weight rows), from a sweep on
@@ -1061,7 +1063,10 @@ static hipError_t launch_expert_mx(const P& p, const Tile* tiles, const int* nti
 // 2 GiB its buffer offsets reach: gathered rows (up projection) lie less than
 // the token count, itself at most the slot count (below max_tiles * tile
 // rows), rows after it; rows read in place (down projection) lie within the
-// tile's 128.
+// tile's 128.  Wave layout, measured at the prefill batch (T = 8192, both
+// layouts give the same bits): 1 x 8 takes the down projection from 3.38 to
+// 3.28 ms; on the up projection the two are within run-to-run noise (3.44 to
+// 3.51 ms), and 2 x 4 keeps its skip of the MFMAs of a half tile with no rows.
 template <class P>
 static hipError_t launch_lds_mx(const P& p, const Tile* tiles, const int* ntiles, int max_tiles,
                                 hipStream_t s) {
@@ -1070,7 +1075,7 @@ static hipError_t launch_lds_mx(const P& p, const Tile* tiles, const int* ntiles
       a_span < (1L << 31)) {
     const long grid = xcd_grid((long)max_tiles * (p.N() / 512));
     if (grid <= 0) return hipSuccess;
-    lds_mx_kernel<P, kExpBM, 512><<<grid, 512, 0, s>>>(p, tiles, ntiles);
+    lds_mx_kernel<P, kExpBM, 512, P::kGatherA ? 2 : 1><<<grid, 512, 0, s>>>(p, tiles, ntiles);
     return hipGetLastError();
   }
   return launch_expert_mx(p, tiles, ntiles, max_tiles, s);
