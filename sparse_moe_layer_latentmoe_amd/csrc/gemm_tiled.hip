@@ -998,17 +998,21 @@ static int pick_splits(int K, int want) {
 
 // Tile shapes and split counts measured on the full-shape problems at
 // T = 192 (speculative-verify batch), reduction included: output projection
-// 256x256 in 8 splits (59-61 us; 62 vs 145 us for the best weight-streaming
-// shape), latent 128x128 in 8 splits (20.5 us against 26.5-27.1 for 128x256
-// with 3 stages), shared up 128x128 in 4 splits (56.5-57.4 us against
-// 58.1-59.8 for 256x256).  With the same split count the tile shape leaves
-// every output bit unchanged.
+// 192x128 with four stages in 4 splits (52-53 us against 61-63 for 256x256
+// in 8 splits and 145 for the best weight-streaming shape: one tile covers
+// the batch's rows, and three stages are in flight), latent 128x128 in 8
+// splits (20.5 us against 26.5-27.1 for 128x256 with 3 stages; 192-row tiles
+// within 1 us), shared up 128x128 in 4 splits (56.5-57.4 us against
+// 58.1-59.8 for 256x256, 56-63 for 192x128).  With the same split count the
+// tile shape leaves every output bit unchanged.
 hipError_t split_proj_in(const ProjIn& p, float* part, hipStream_t s) {
   if (p.N() <= 4096)
     return launch_split<ProjIn, 128, 128, 2>(p, p.T, part, pick_splits(p.K(), kSplitMax), s);
   return launch_split<ProjIn, 128, 128, 2>(p, p.T, part, pick_splits(p.K(), 4), s);
 }
 hipError_t split_proj_out(const ProjOut& p, float* part, hipStream_t s) {
+  if (p.T <= 192 && p.N() % 128 == 0)
+    return launch_split<ProjOut, 192, 128, 4>(p, p.T, part, pick_splits(p.K(), 4), s);
   return launch_split<ProjOut, 256, 256, 2>(p, p.T, part, pick_splits(p.K(), kSplitMax), s);
 }
 

@@ -24,23 +24,28 @@ def dev():
     return torch.device("cuda:0")
 
 
-@pytest.mark.parametrize("shape,tokens,path", [
-    (li.TINY, 64, pkg.PATH_AUTO),        # weight-streaming GEMMs
-    (MEDIUM, 300, pkg.PATH_AUTO),        # LDS-tiled GEMMs
+# warm: one eager forward on a side stream before the capture; cold: the
+# handle's first forward is the captured one (the auxiliary stream and its
+# events already exist, created with the handle)
+@pytest.mark.parametrize("shape,tokens,path,warm", [
+    (li.TINY, 64, pkg.PATH_AUTO, False),        # weight-streaming GEMMs
+    (MEDIUM, 300, pkg.PATH_AUTO, False),        # LDS-tiled GEMMs
+    (MEDIUM, 300, pkg.PATH_AUTO, True),
 ])
-def test_captured_forward_replays_match_eager(dev, shape, tokens, path):
-    print(f"[graph D={shape.hidden_size} T={tokens} path={path}]", flush=True)
+def test_captured_forward_replays_match_eager(dev, shape, tokens, path, warm):
+    print(f"[graph D={shape.hidden_size} T={tokens} path={path} warm={warm}]", flush=True)
     sys.stdout.flush()
     wl = li.Workload("graph", shape, tokens)
     inp = li.make_inputs(wl, dev)
     layer = pkg.LatentMoE(shape, weight_dict(inp), tokens, path=path)
     x = inp.x.clone()
     y = torch.empty_like(x)
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        layer.forward_into(x, y)          # first forward: creates the auxiliary stream
-    torch.cuda.current_stream().wait_stream(side)
+    if warm:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            layer.forward_into(x, y)
+        torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
