@@ -33,6 +33,7 @@ struct ProjIn {
   int noff, ncount;
   const float* rscale;  // [T] or null
   static constexpr bool kGatherA = false;
+  static constexpr bool kStagedStore = false;
   __device__ const uint16_t* a_base0() const { return x; }
   __device__ const uint16_t* a_base1() const { return x; }
   __device__ long lda0() const { return D; }
@@ -80,6 +81,7 @@ struct ProjOut {
   int part = 0;
   float* ys = nullptr;    // [T, D] fp32 for parts 1 and 2
   static constexpr bool kGatherA = false;
+  static constexpr bool kStagedStore = false;
   __device__ const uint16_t* a_base0() const { return part == 1 ? hs : r16; }
   __device__ const uint16_t* a_base1() const { return hs; }
   __device__ long lda0() const { return part == 1 ? S : R; }
@@ -145,6 +147,13 @@ struct ExpUp {
   __device__ void store_nt(int, int p, int n, f32x4 v) const {
     store4_bf16_relu_sq_nt(h + (size_t)p * F + n, v);
   }
+  // the same values in two steps, for output staged through LDS: pack4
+  // gives the stored bits of four columns, store8 writes eight columns
+  static constexpr bool kStagedStore = true;
+  __device__ u16x4 pack4(f32x4 v) const { return pack4_bf16_relu_sq(v); }
+  __device__ void store8(int p, int n, u16x8 v) const {
+    *reinterpret_cast<u16x8*>(h + (size_t)p * F + n) = v;
+  }
 };
 
 // Expert down projection (Step 6): O[p] = H[p] Wdn[e]^T, stored bf16; the
@@ -176,6 +185,11 @@ struct ExpDown {
   __device__ void store_nt(int, int p, int n, f32x4 v) const {
     store4_bf16_nt(o + (size_t)p * R + n, v);
   }
+  static constexpr bool kStagedStore = true;
+  __device__ u16x4 pack4(f32x4 v) const { return pack4_bf16(v); }
+  __device__ void store8(int p, int n, u16x8 v) const {
+    *reinterpret_cast<u16x8*>(o + (size_t)p * R + n) = v;
+  }
 };
 
 // Expert GEMMs with MXFP4 weights (block-scaled FP4; the layout of
@@ -202,6 +216,11 @@ struct ExpUpMx {
   __device__ void store(int, int p, int n, f32x4 v) const {
     store4_bf16_relu_sq(h + (size_t)p * F + n, v);
   }
+  static constexpr bool kStagedStore = true;
+  __device__ u16x4 pack4(f32x4 v) const { return pack4_bf16_relu_sq(v); }
+  __device__ void store8(int p, int n, u16x8 v) const {
+    *reinterpret_cast<u16x8*>(h + (size_t)p * F + n) = v;
+  }
 };
 
 struct ExpDownMx {
@@ -223,6 +242,11 @@ struct ExpDownMx {
   __device__ void store(int, int p, int n, f32x4 v) const {
     store4_bf16(o + (size_t)p * R + n, v);
   }
+  static constexpr bool kStagedStore = true;
+  __device__ u16x4 pack4(f32x4 v) const { return pack4_bf16(v); }
+  __device__ void store8(int p, int n, u16x8 v) const {
+    *reinterpret_cast<u16x8*>(o + (size_t)p * R + n) = v;
+  }
 };
 
 // Split-k view of a dense problem for the LDS-tiled kernel: work-group
@@ -240,6 +264,7 @@ struct SplitK {
   float* part;
   int mrows;
   static constexpr bool kGatherA = P::kGatherA;
+  static constexpr bool kStagedStore = false;
   __device__ int kstart() const { return blockIdx.y * klen; }
   __device__ int off1() const {
     const int v = kstart() - p.K0();

@@ -46,6 +46,43 @@ __device__ __forceinline__ void stage_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Output of one wave's block of 16 TM rows, written through LDS.  In the
+// MFMA result layout lane (r, q) (r = lane % 16, q = lane / 16) of tile
+// (g, t) holds columns 16 g + 4 q .. + 3 of row 16 t + r, so a direct store
+// instruction writes 16 pieces of 32 bytes.  Here tiles G0 .. G0 + GN - 1
+// are packed (p.pack4: the stored bits of four columns) into `reg`, the
+// wave's own LDS region of 16 TM rows x 32 GN bytes (16-byte chunks XOR-
+// swizzled by row), and read back as 16 contiguous bytes per lane, so that
+// each store instruction (p.store8) writes whole 32 GN-byte row pieces.
+// Rows from `rows` on are not stored; row i goes to slot m0 + i, columns
+// from n0.  Only this wave touches `reg`, and a wave's LDS accesses stay in
+// order, so no barrier is needed inside.  Measured on the prefill batch's
+// expert GEMMs (bitwise equal): MXFP4 up projection 3.41 against 3.45-3.56
+// ms with direct stores, down projection 3.18 against 3.30-3.33 ms.
+template <int GN, int G0, int TN, int TM, class P>
+__device__ __forceinline__ void staged_store(const P& p, char* reg, int lane,
+                                             const f32x4 (&acc)[TN][TM], int m0, int rows, int n0) {
+  constexpr int RB = GN * 32, CH = RB / 16, RPI = 64 / CH;
+  static_assert(G0 + GN <= TN && (CH & (CH - 1)) == 0 && CH <= 64, "staged store");
+  const int r16 = lane & 15, kq = lane >> 4;
+#pragma unroll
+  for (int g = 0; g < GN; ++g)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      const int row = t * 16 + r16;
+      const int chunk = 2 * g + (kq >> 1);
+      *reinterpret_cast<u16x4*>(reg + row * RB + ((chunk ^ (row & (CH - 1))) << 4) +
+                                (kq & 1) * 8) = p.pack4(acc[G0 + g][t]);
+    }
+  const int c = lane & (CH - 1);
+#pragma unroll
+  for (int j = 0; j < 16 * TM / RPI; ++j) {
+    const int row = j * RPI + lane / CH;
+    const u16x8 v = *reinterpret_cast<const u16x8*>(reg + row * RB + ((c ^ (row & (CH - 1))) << 4));
+    if (row < rows) p.store8(m0 + row, n0 + c * 8, v);
+  }
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Work-item order.  Work-groups are dealt to the 8 XCDs round-robin by id,
@@ -262,6 +299,17 @@ __global__ __launch_bounds__(128 * WGN) void tiled_gemm_kernel(P p, int mrows, c
     kloop(std::false_type{});
   }
 
+  if constexpr (GROUPED && P::kStagedStore && NS == 2 && TN == 8 && TM == 4) {
+    // through the stage buffer the last k tile did not read (its last
+    // reader, tile nk - 2, finished before every wave passed tile nk - 1's
+    // barrier; no copy targets it any more): 8 KB per wave, two passes of
+    // 64 columns
+    char* const reg = reinterpret_cast<char*>(&smem[nk % 2][0]) + w * (64 * 128);
+    const int wr = wm * (BM / 2), wc = n0 + wn * (BN / WGN);
+    staged_store<4, 0>(p, reg, lane, acc, m0 + wr, mcount - wr, wc);
+    staged_store<4, 4>(p, reg, lane, acc, m0 + wr, mcount - wr, wc + 64);
+    return;
+  }
   const int ncol = (lane >> 4) * 4;
 #pragma unroll
   for (int gi = 0; gi < TN; ++gi)
@@ -556,6 +604,16 @@ __device__ __forceinline__ void lds_gemm_body(const P& p, int mrows, const Tile*
   }
   run(body);
 
+  if constexpr (GROUPED && P::kStagedStore && TN == 8 && TM == 4) {
+    // through stage buffer 0, which the last k tile (buffer 1) does not read
+    // and whose last reader finished before every wave passed that tile's
+    // barrier: 8 KB per wave, two passes of 64 columns
+    char* const reg = smem + w * (64 * 128);
+    const int wr = wm * (BM / WM), wc = n0 + wn * (BN / WN);
+    staged_store<4, 0>(p, reg, lane, acc, m0 + wr, mcount - wr, wc);
+    staged_store<4, 4>(p, reg, lane, acc, m0 + wr, mcount - wr, wc + 64);
+    return;
+  }
   const int ncol = (lane >> 4) * 4;
 #pragma unroll
   for (int g = 0; g < TN; ++g)
@@ -899,6 +957,15 @@ __device__ __forceinline__ void lds_mx_body(const P& p, const Tile* tiles, const
   }
   run(body);
 
+  if constexpr (P::kStagedStore && WM == 1) {
+    // 16 KB per wave over both stage buffers, after a barrier (every wave
+    // is done reading them; with WM = 1 every wave has rows, so every wave
+    // of the work-group reaches it)
+    static_assert(BN / WN == 64 && TN == 4 && BM * 128 * NW <= 2 * STAGE, "staged store");
+    stage_barrier_hard();
+    staged_store<4, 0>(p, smem + w * (BM * 128), lane, acc, m0, mcount, n0 + wn * 64);
+    return;
+  }
   const int ncol = (lane >> 4) * 4;
 #pragma unroll
   for (int g = 0; g < TN; ++g)
@@ -1067,10 +1134,11 @@ static hipError_t launch_expert_mx(const P& p, const Tile* tiles, const int* nti
 // 2 GiB its buffer offsets reach: gathered rows (up projection) lie less than
 // the token count, itself at most the slot count (below max_tiles * tile
 // rows), rows after it; rows read in place (down projection) lie within the
-// tile's 128.  Wave layout, measured at the prefill batch (T = 8192, both
-// layouts give the same bits): 1 x 8 takes the down projection from 3.38 to
-// 3.28 ms; on the up projection the two are within run-to-run noise (3.44 to
-// 3.51 ms), and 2 x 4 keeps its skip of the MFMAs of a half tile with no rows.
+// tile's 128.  Wave layout 1 x 8, whose 128 x 64 blocks go out through LDS
+// (staged_store).  Measured at the prefill batch (T = 8192, all three give the
+// same bits), with direct stores 1 x 8 took the down projection from 3.38 to
+// 3.28 ms and left the up projection within run-to-run noise (3.44 to 3.51
+// ms for both layouts).
 template <class P>
 static hipError_t launch_lds_mx(const P& p, const Tile* tiles, const int* ntiles, int max_tiles,
                                 hipStream_t s) {
@@ -1079,7 +1147,7 @@ static hipError_t launch_lds_mx(const P& p, const Tile* tiles, const int* ntiles
       a_span < (1L << 31)) {
     const long grid = xcd_grid((long)max_tiles * (p.N() / 512));
     if (grid <= 0) return hipSuccess;
-    lds_mx_kernel<P, kExpBM, 512, P::kGatherA ? 2 : 1><<<grid, 512, 0, s>>>(p, tiles, ntiles);
+    lds_mx_kernel<P, kExpBM, 512, 1><<<grid, 512, 0, s>>>(p, tiles, ntiles);
     return hipGetLastError();
   }
   return launch_expert_mx(p, tiles, ntiles, max_tiles, s);

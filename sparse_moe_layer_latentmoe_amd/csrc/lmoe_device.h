@@ -8,6 +8,7 @@ namespace lmoe {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
 // bfloat16 is the high half of an IEEE float32.
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
@@ -54,42 +55,40 @@ __device__ __forceinline__ bf16x8 zero8() {
   return z;
 }
 
-// Store four consecutive fp32 values as bfloat16 (8-byte store).
-__device__ __forceinline__ void store4_bf16(uint16_t* p, f32x4 v) {
+// Four fp32 values rounded to bfloat16 (relu^2 first for the second form).
+__device__ __forceinline__ u16x4 pack4_bf16(f32x4 v) {
   u16x4 o;
   o[0] = f32_to_bf16(v[0]);
   o[1] = f32_to_bf16(v[1]);
   o[2] = f32_to_bf16(v[2]);
   o[3] = f32_to_bf16(v[3]);
-  *reinterpret_cast<u16x4*>(p) = o;
+  return o;
+}
+__device__ __forceinline__ u16x4 pack4_bf16_relu_sq(f32x4 v) {
+  f32x4 a;
+  a[0] = relu_sq(v[0]);
+  a[1] = relu_sq(v[1]);
+  a[2] = relu_sq(v[2]);
+  a[3] = relu_sq(v[3]);
+  return pack4_bf16(a);
+}
+
+// Store four consecutive fp32 values as bfloat16 (8-byte store).
+__device__ __forceinline__ void store4_bf16(uint16_t* p, f32x4 v) {
+  *reinterpret_cast<u16x4*>(p) = pack4_bf16(v);
 }
 
 // The same with the non-temporal hint.
 __device__ __forceinline__ void store4_bf16_nt(uint16_t* p, f32x4 v) {
-  u16x4 o;
-  o[0] = f32_to_bf16(v[0]);
-  o[1] = f32_to_bf16(v[1]);
-  o[2] = f32_to_bf16(v[2]);
-  o[3] = f32_to_bf16(v[3]);
-  __builtin_nontemporal_store(o, reinterpret_cast<u16x4*>(p));
+  __builtin_nontemporal_store(pack4_bf16(v), reinterpret_cast<u16x4*>(p));
 }
 
 __device__ __forceinline__ void store4_bf16_relu_sq(uint16_t* p, f32x4 v) {
-  f32x4 a;
-  a[0] = relu_sq(v[0]);
-  a[1] = relu_sq(v[1]);
-  a[2] = relu_sq(v[2]);
-  a[3] = relu_sq(v[3]);
-  store4_bf16(p, a);
+  *reinterpret_cast<u16x4*>(p) = pack4_bf16_relu_sq(v);
 }
 
 __device__ __forceinline__ void store4_bf16_relu_sq_nt(uint16_t* p, f32x4 v) {
-  f32x4 a;
-  a[0] = relu_sq(v[0]);
-  a[1] = relu_sq(v[1]);
-  a[2] = relu_sq(v[2]);
-  a[3] = relu_sq(v[3]);
-  store4_bf16_nt(p, a);
+  __builtin_nontemporal_store(pack4_bf16_relu_sq(v), reinterpret_cast<u16x4*>(p));
 }
 
 // Work tile of the grouped expert GEMMs: rows [row0, row0 + nrows) of the
