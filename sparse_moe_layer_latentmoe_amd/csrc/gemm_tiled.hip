@@ -339,9 +339,11 @@ __global__ __launch_bounds__(128 * WGN) void tiled_gemm_kernel(P p, int mrows, c
 //  - a wave whose token rows all lie past the tile's count only copies.
 // Measured on the prefill batch's problems (standalone, same inputs): expert
 // up 4.60 -> 4.43 ms, shared up 1.13 -> 1.03 ms (with the directed MFMA /
-// LDS-read interleave, SCHED = 1); expert down 4.50 -> 4.60 ms, so the down
-// projection keeps tiled_gemm_kernel.  Launched when the k range is an even
-// number of 64-wide k tiles (every full-shape problem).
+// LDS-read interleave, SCHED = 1); expert down 4.50 -> 4.60 ms at first, and
+// 4.54 -> 4.46 ms once both kernels wrote their outputs through LDS
+// (staged_store), so both expert projections now take it.  Launched when
+// the k range is an even number of 64-wide k tiles (every full-shape
+// problem).
 
 // Problems whose k range has two segments (the output projection's [r | Hs]).
 template <class P>
@@ -1111,8 +1113,16 @@ hipError_t tiled_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, in
   }
   return launch_expert(p, tiles, ntiles, max_tiles, s);
 }
+// Expert down projection: lds_gemm_kernel too when N allows 512-row weight
+// tiles (its token rows are read in place, within the tile's 128).
 hipError_t tiled_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles, int max_tiles,
                           hipStream_t s) {
+  if (p.N() % 512 == 0 && p.K() % 128 == 0) {
+    const long grid = xcd_grid((long)max_tiles * (p.N() / 512));
+    if (grid <= 0) return hipSuccess;
+    lds_gemm_kernel<ExpDown, true, kExpBM, 512, 0><<<grid, 512, 0, s>>>(p, 0, tiles, ntiles);
+    return hipGetLastError();
+  }
   return launch_expert(p, tiles, ntiles, max_tiles, s);
 }
 
