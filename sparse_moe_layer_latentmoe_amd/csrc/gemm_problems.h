@@ -154,6 +154,9 @@ struct ExpUp {
   __device__ void store8(int p, int n, u16x8 v) const {
     *reinterpret_cast<u16x8*>(h + (size_t)p * F + n) = v;
   }
+  __device__ void store8_nt(int p, int n, u16x8 v) const {
+    __builtin_nontemporal_store(v, reinterpret_cast<u16x8*>(h + (size_t)p * F + n));
+  }
 };
 
 // Expert down projection (Step 6): O[p] = H[p] Wdn[e]^T, stored bf16; the
@@ -189,6 +192,9 @@ struct ExpDown {
   __device__ u16x4 pack4(f32x4 v) const { return pack4_bf16(v); }
   __device__ void store8(int p, int n, u16x8 v) const {
     *reinterpret_cast<u16x8*>(o + (size_t)p * R + n) = v;
+  }
+  __device__ void store8_nt(int p, int n, u16x8 v) const {
+    __builtin_nontemporal_store(v, reinterpret_cast<u16x8*>(o + (size_t)p * R + n));
   }
 };
 

@@ -189,6 +189,40 @@ __global__ __launch_bounds__(NW * 64) void stream_gemm_kernel(P p, int mrows, co
         const int i = t * 16 + r16;
         if (i < mcount) store(m0 + i, n0 + g * 16 + ncol, acc[g][t]);
       }
+  } else if constexpr (GROUPED && MT == 1 && (RG == 2 || RG == 4) && P::kStagedStore) {
+    // Wave 0 adds the waves' partial sums of all RG tiles and writes the
+    // tile's 16 rows x 16 RG columns through LDS (red[0], already read), so
+    // that each lane stores 16 contiguous bytes and each instruction whole
+    // 32 RG-byte row pieces (in the MFMA layout a store instruction writes
+    // 16 pieces of 32 bytes).
+#pragma unroll
+    for (int g = 0; g < RG; ++g) red[w][g][lane] = acc[g][0];
+    __syncthreads();
+    if (w == 0) {
+      constexpr int RB = 32 * RG, CH = RB / 16, RPI = 64 / CH;
+      f32x4 sm[RG];
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        sm[g] = red[0][g][lane];
+#pragma unroll
+        for (int v = 1; v < NW; ++v) sm[g] += red[v][g][lane];
+      }
+      char* const reg = reinterpret_cast<char*>(&red[0][0][0]);
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        const int chunk = 2 * g + (kq >> 1);
+        *reinterpret_cast<u16x4*>(reg + r16 * RB + ((chunk ^ (r16 & (CH - 1))) << 4) +
+                                  (kq & 1) * 8) = p.pack4(sm[g]);
+      }
+      const int c = lane & (CH - 1);
+#pragma unroll
+      for (int j = 0; j < 16 / RPI; ++j) {
+        const int i = j * RPI + lane / CH;
+        const u16x8 v =
+            *reinterpret_cast<const u16x8*>(reg + i * RB + ((c ^ (i & (CH - 1))) << 4));
+        if (i < mcount) p.store8_nt(m0 + i, n0 + c * 8, v);
+      }
+    }
   } else {
 #pragma unroll
     for (int g = 0; g < RG; ++g)
