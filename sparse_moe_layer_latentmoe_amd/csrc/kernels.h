@@ -52,8 +52,9 @@ hipError_t split_proj_out(const ProjOut& p, float* part, hipStream_t s);
 // expert GEMMs (K a multiple of 128, N a multiple of 64).
 hipError_t mxfp4_quantize(const uint16_t* w, long rows, int cols, uint8_t* codes,
                           uint8_t* scales, hipStream_t s);
+// rows_per_expert as for stream_exp_down
 hipError_t stream_mx_exp_up(const ExpUpMx& p, const Tile* tiles, const int* ntiles,
-                            int max_tiles, hipStream_t s);
+                            int max_tiles, int rows_per_expert, hipStream_t s);
 hipError_t stream_mx_exp_down(const ExpDownMx& p, const Tile* tiles, const int* ntiles,
                               int max_tiles, hipStream_t s);
 // The LDS-tiled expert GEMMs with MXFP4 weights (large batches; same

@@ -206,21 +206,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base) {
 
 }  // namespace
 
-// Grouped expert GEMM for K a multiple of 512 and N of 128 (codes and scales
-// 16-byte aligned).  Work-group = 4 waves on one 16-row token tile and 128
-// weight rows, each wave 2 row groups (32 rows) over the whole k range, in
-// stages of 256 k (8 waves on 256 rows measured 1-2% slower: 332 vs 324 us
-// for the decode batch's down projection).  Everything a stage needs from memory arrives by direct
-// global -> LDS loads issued one stage ahead:
-//  - each wave copies its own 32 rows' codes of the stage (32 x 128 bytes,
-//    four loads of 8 whole lines) with the non-temporal hint into its own two
+// Grouped expert GEMM for K a multiple of 512 and N of 16 NW RG (codes and
+// scales 16-byte aligned).  Work-group = NW waves on one 16-row token tile
+// and 16 NW RG weight rows, each wave RG row groups (16 RG rows) over the
+// whole k range, in stages of 256 k (launched with 4 waves of 2 or 4 row
+// groups; 8 waves on 256 rows measured 1-2% slower: 332 vs 324 us for the
+// decode batch's down projection).  Everything a stage needs from memory
+// arrives by direct global -> LDS loads issued one stage ahead:
+//  - each wave copies its own rows' codes of the stage (16 RG x 128 bytes,
+//    2 RG loads of 8 whole lines) with the non-temporal hint into its own two
 //    LDS slots.  Measured on the decode batch's up-projection codes with no
 //    arithmetic: 7.1 TB/s, the read ceiling of the chip, against 6.2-6.3 TB/s
 //    for these bytes loaded into registers 16 rows x 64 bytes at a time (the
 //    MFMA layout, both halves of a line back to back) and 6.2-6.3 without the
 //    hint;
 //  - the stage's token tile (16 rows x 512 bytes) is copied by the whole
-//    work-group, two loads per wave;
+//    work-group, 8 / NW loads per wave;
 //  - the scale bytes of a pair of stages come in one 16-byte register load per
 //    row, one pair ahead.
 // One barrier per stage.  LDS rows are XOR-swizzled: code row r keeps its
@@ -228,11 +229,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base) {
 // items (tile, row block) are taken XCD-major.  The products and their order
 // are those of the general kernel's k assignment: lane (r, q) of step u in
 // half h of a stage takes code bytes 4u..4u+3 of block 4h + q of row r.
-// 48 KB of LDS per work-group, three work-groups per CU.
-template <class P>
+// LDS per work-group: 48 KB with 4 waves of 2 row groups (three work-groups
+// per CU), 80 KB with 4 of 4 (two).
+template <class P, int NW, int RG>
 __device__ __forceinline__ void stream_mx_lds_body(const P& p, const Tile* tiles,
                                                    const int* ntiles) {
-  constexpr int NW = 4, RG = 2, ROWS = NW * 16 * RG;
+  constexpr int ROWS = NW * 16 * RG;
+  static_assert(8 % NW == 0 && NW * 2 * 16 * RG * 128 + 2 * 16 * 512 <= 160 * 1024, "shape");
   constexpr int CSLOT = 16 * RG * 128;  // one wave's codes of one stage
   constexpr int TSLOT = 16 * 512;       // the token tile of one stage
   constexpr int TPW = 8 / NW;           // token loads (2 rows each) per wave
@@ -341,10 +344,10 @@ __device__ __forceinline__ void stream_mx_lds_body(const P& p, const Tile* tiles
     if (r16 < mcount) p.store(e, m0 + r16, n0 + g * 16 + ncol, acc[g]);
 }
 
-template <class P>
-__global__ __launch_bounds__(256) void stream_mx_lds_kernel(P p, const Tile* tiles,
-                                                            const int* ntiles) {
-  stream_mx_lds_body<P>(p, tiles, ntiles);
+template <class P, int NW, int RG>
+__global__ __launch_bounds__(NW * 64) void stream_mx_lds_kernel(P p, const Tile* tiles,
+                                                                const int* ntiles) {
+  stream_mx_lds_body<P, NW, RG>(p, tiles, ntiles);
 }
 
 // stream_mx_lds_kernel where its conditions hold (K a multiple of 512, N of
@@ -355,15 +358,27 @@ __global__ __launch_bounds__(256) void stream_mx_lds_kernel(P p, const Tile* til
 // otherwise the general kernel with the largest of 4, 2, 1 waves per
 // work-group whose k share is a whole number of 128-k steps (K is a multiple
 // of 128).
+// Four waves of two row groups (128 weight rows per work-group), or of four
+// (256) when `wide` and N allows it: each work-group copies its tile's token
+// rows once per stage, and with ~8 rows per expert those are a third of its
+// bytes; measured standalone (us, T = 32 / T = 192): up projection 322-325 /
+// 500-501 with two, 327-328 / 483-484 with four; down projection 328 / 473
+// with two, 337 / 472 with four; eight waves of two or four were no better.
 template <class P>
 static hipError_t launch_mx(const P& p, const Tile* tiles, const int* ntiles, int max_tiles,
-                            hipStream_t s) {
+                            bool wide, hipStream_t s) {
   const bool aligned = ((reinterpret_cast<uintptr_t>(p.codes) | reinterpret_cast<uintptr_t>(p.scales)) & 15) == 0;
   const long a_span = (P::kGatherA ? (long)max_tiles * 16 : 16L) * p.K() * 2;
   if (p.K() % 512 == 0 && p.N() % 128 == 0 && aligned && a_span < (1L << 31)) {
+    if (wide && p.N() % 256 == 0) {
+      const long grid = (long)max_tiles * (p.N() / 256);
+      if (grid <= 0) return hipSuccess;
+      stream_mx_lds_kernel<P, 4, 4><<<grid, 256, 0, s>>>(p, tiles, ntiles);
+      return hipGetLastError();
+    }
     const long grid = (long)max_tiles * (p.N() / 128);
     if (grid <= 0) return hipSuccess;
-    stream_mx_lds_kernel<P><<<grid, 256, 0, s>>>(p, tiles, ntiles);
+    stream_mx_lds_kernel<P, 4, 2><<<grid, 256, 0, s>>>(p, tiles, ntiles);
     return hipGetLastError();
   }
   constexpr int RG = 4;
@@ -379,12 +394,12 @@ static hipError_t launch_mx(const P& p, const Tile* tiles, const int* ntiles, in
 }
 
 hipError_t stream_mx_exp_up(const ExpUpMx& p, const Tile* tiles, const int* ntiles,
-                            int max_tiles, hipStream_t s) {
-  return launch_mx(p, tiles, ntiles, max_tiles, s);
+                            int max_tiles, int rows_per_expert, hipStream_t s) {
+  return launch_mx(p, tiles, ntiles, max_tiles, rows_per_expert > 2, s);
 }
 hipError_t stream_mx_exp_down(const ExpDownMx& p, const Tile* tiles, const int* ntiles,
                               int max_tiles, hipStream_t s) {
-  return launch_mx(p, tiles, ntiles, max_tiles, s);
+  return launch_mx(p, tiles, ntiles, max_tiles, false, s);
 }
 
 }  // namespace lmoe
