@@ -88,10 +88,10 @@ typedef enum { LMOE_PATH_AUTO = 0, LMOE_PATH_STREAM = 1, LMOE_PATH_TILED = 2 } l
  * MXFP4 (block-scaled FP4 with the E2M1 elements of CH8 §8.1 of the page
  * "Nemotron 3 Ultra 架构深度拆解报告"; block layout: lmoe_quantize_mxfp4):
  * the *_mxfp4 / *_scale fields; the expert GEMMs decode the weights exactly
- * to bf16, streaming them for small batches and decoding them into the
- * LDS-tiled GEMM's weight tiles for large ones (the same lmoe_path choice as
- * bf16 weights; R and F must be multiples of 128).  Everything else stays
- * bf16 / fp32. */
+ * to bf16, streaming them for small batches and, for large ones, copying
+ * the FP4 codes into the LDS-tiled GEMM's tiles and decoding them right
+ * before the MFMAs (the same lmoe_path choice as bf16 weights; R and F must
+ * be multiples of 128).  Everything else stays bf16 / fp32. */
 typedef enum { LMOE_EXPERTS_BF16 = 0, LMOE_EXPERTS_MXFP4 = 1 } lmoe_expert_format;
 
 /* Block steps fused into the layer (bits of lmoe_config.fuse; CH9 §9.3 of
