@@ -20,7 +20,8 @@
 //
 // Work order is XCD-aware (see work_item).  Grouped mode (experts) takes the
 // m tiles from the expert tile list built by the dispatch kernel; a tile
-// never spans two experts.
+// never spans two experts, and its output goes out through LDS as whole row
+// pieces (staged_store).
 #include <type_traits>
 
 #include "gemm_problems.h"
