@@ -495,6 +495,14 @@ __device__ __forceinline__ void lds_gemm_body(const P& p, int mrows, const Tile*
   const uint32_t aw = (uint32_t)(wm * (BM / WM)) * ROWB;
   const uint32_t bw = (uint32_t)(BM + wn * (BN / WN)) * ROWB;
   const bool has_rows = wm * (BM / WM) < mcount;
+  // 16-row token groups of this wave that hold rows (uniform): expert tiles
+  // skip the MFMAs of the others (scalar branches; the fragment reads stay
+  // unconditional).  At the prefill batch, where padding rows are 8.7% of
+  // the MFMA work otherwise: expert up 4.22-4.24 -> 4.14-4.16 ms, down
+  // 4.43-4.44 -> 4.36 ms standalone, same bits.  (The same skip in
+  // lds_mx_kernel made it slower: up 3.41-3.46 -> 3.55-3.61 ms, down
+  // 3.23-3.25 -> 3.61 ms.)
+  const int tlim = uniform(min(TM, max(0, (mcount - wm * (BM / WM) + 15) / 16)));
 
   f32x4 acc[TN][TM];
 #pragma unroll
@@ -529,8 +537,9 @@ __device__ __forceinline__ void lds_gemm_body(const P& p, int mrows, const Tile*
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int t = 0; t < TM; ++t)
+        if (!GROUPED || t < tlim)
 #pragma unroll
-        for (int g = 0; g < TN; ++g) acc[g][t] = mfma_bf16(wf[ks][g], xf[ks][t], acc[g][t]);
+          for (int g = 0; g < TN; ++g) acc[g][t] = mfma_bf16(wf[ks][g], xf[ks][t], acc[g][t]);
     if constexpr (SCHED == 1) {
       // directed order: the first half's fragment reads, the copies spread
       // over the first MFMAs, the second half's reads under the rest of the
