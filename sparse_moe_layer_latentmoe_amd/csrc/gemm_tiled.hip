@@ -499,9 +499,8 @@ __device__ __forceinline__ void lds_gemm_body(const P& p, int mrows, const Tile*
   // skip the MFMAs of the others (scalar branches; the fragment reads stay
   // unconditional).  At the prefill batch, where padding rows are 8.7% of
   // the MFMA work otherwise: expert up 4.22-4.24 -> 4.14-4.16 ms, down
-  // 4.43-4.44 -> 4.36 ms standalone, same bits.  (The same skip in
-  // lds_mx_kernel made it slower: up 3.41-3.46 -> 3.55-3.61 ms, down
-  // 3.23-3.25 -> 3.61 ms.)
+  // 4.43-4.44 -> 4.36 ms standalone, same bits.  (lds_mx_kernel, where the
+  // same branch was slower, takes one of four copies of its k loop instead.)
   const int tlim = uniform(min(TM, max(0, (mcount - wm * (BM / WM) + 15) / 16)));
 
   f32x4 acc[TN][TM];
@@ -906,8 +905,9 @@ __device__ __forceinline__ void lds_mx_body(const P& p, const Tile* tiles, const
 
   // step kt (buffer BUF = kt % 2, Q = kt % 4): copy stage kt + 1 (and, when
   // it starts a group of 4, that group's scales) unless COPY is false
-  auto body = [&](auto q_c, auto copy_c, int kt) __attribute__((always_inline)) {
+  auto body_ta = [&](auto q_c, auto copy_c, int kt, auto ta_c) __attribute__((always_inline)) {
     constexpr int Q = decltype(q_c)::value, BUF = Q & 1;
+    constexpr int TA = decltype(ta_c)::value;  // token groups computed
     wait_vmcnt<0>();
     stage_barrier_hard();
     if constexpr (decltype(copy_c)::value) issue(kt + 1, BUF ^ 1, Q == 3);
@@ -922,18 +922,25 @@ __device__ __forceinline__ void lds_mx_body(const P& p, const Tile* tiles, const
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      bf16x8 xf[TM];
+      bf16x8 xf[TA];
 #pragma unroll
-      for (int t = 0; t < TM; ++t)
+      for (int t = 0; t < TA; ++t)
         xf[t] = *reinterpret_cast<const bf16x8*>(st + ard + t * 16 * AROW +
                                                  ((((kq << 2) + s) ^ r16) << 4));
 #pragma unroll
       for (int g = 0; g < TN; ++g) {
         const bf16x8 wf = mx_decode8(code[g][s], sc[g]);
 #pragma unroll
-        for (int t = 0; t < TM; ++t) acc[g][t] = mfma_bf16(wf, xf[t], acc[g][t]);
+        for (int t = 0; t < TA; ++t) acc[g][t] = mfma_bf16(wf, xf[t], acc[g][t]);
       }
     }
+  };
+  // the step computing the first TA token groups only (the wave's rows past
+  // them are padding of the tile)
+  auto body_of = [&](auto ta_c) __attribute__((always_inline)) {
+    return [&, ta_c](auto q_c, auto copy_c, int kt) __attribute__((always_inline)) {
+      body_ta(q_c, copy_c, kt, ta_c);
+    };
   };
   auto copy_only = [&](auto q_c, auto copy_c, int kt) __attribute__((always_inline)) {
     constexpr int Q = decltype(q_c)::value, BUF = Q & 1;
@@ -967,7 +974,25 @@ __device__ __forceinline__ void lds_mx_body(const P& p, const Tile* tiles, const
     run(copy_only);
     return;
   }
-  run(body);
+  // With one wave along the tokens every wave computes all BM rows, so a
+  // partly filled tile takes one of four copies of the k loop: the first
+  // quarter, half, three quarters or all of its token groups.  Measured at
+  // the prefill batch (same bits): up projection 3.40-3.41 -> 3.19-3.22 ms,
+  // down 3.24-3.26 -> 3.13-3.14 ms (halves only: 3.24-3.25 and 3.14-3.18).
+  // (Skipping each padding group's MFMAs by a branch inside the step
+  // instead was slower than computing them: 3.55-3.61 and 3.61 ms.)
+  if constexpr (WM == 1 && TM % 4 == 0) {
+    if (mcount <= BM / 4)
+      run(body_of(std::integral_constant<int, TM / 4>{}));
+    else if (mcount <= BM / 2)
+      run(body_of(std::integral_constant<int, TM / 2>{}));
+    else if (mcount <= 3 * BM / 4)
+      run(body_of(std::integral_constant<int, 3 * TM / 4>{}));
+    else
+      run(body_of(std::integral_constant<int, TM>{}));
+  } else {
+    run(body_of(std::integral_constant<int, TM>{}));
+  }
 
   if constexpr (P::kStagedStore && WM == 1) {
     // 16 KB per wave over both stage buffers, after a barrier (every wave
