@@ -475,9 +475,15 @@ __device__ __forceinline__ void lds_gemm_body(const P& p, int mrows, const Tile*
   auto issue = [&](const Seg& g, int kb, int buf) __attribute__((always_inline)) {
     char* st = smem + buf * STAGE;
 #pragma unroll
-    for (int j = 0; j < NIA; ++j)
+    for (int j = 0; j < NIA; ++j) {
+      // expert tiles: no copy of token rows wholly past the tile's count
+      // (their LDS rows keep stale values; the outputs of such rows are
+      // never stored, and every wait here is for all copies); at the
+      // prefill batch about 1% faster on both expert projections
+      if (GROUPED && RPI * (w + NW * j) >= mcount) continue;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(g.ra, (lds_void*)(st + (w + NW * j) * RPI * ROWB),
                                                16, g.ao[j], kb, 0, 0);
+    }
 #pragma unroll
     for (int j = 0; j < NIB; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
