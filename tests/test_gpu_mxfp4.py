@@ -105,6 +105,10 @@ def mx_weights(inp):
     (MEDIUM, 1, pkg.PATH_TILED), (MEDIUM, 64, pkg.PATH_TILED), (MX_WIDE, 200, pkg.PATH_TILED),
     (MX_LONG, 1, pkg.PATH_AUTO), (MX_LONG, 37, pkg.PATH_AUTO),
     (MX_DEEP, 150, pkg.PATH_TILED), (MX_DEEP, 3, pkg.PATH_TILED),
+    # ~100 and ~150 rows per expert: the LDS-staged kernel's partly filled
+    # tiles take each of its four k-loop copies (quarter, half, three
+    # quarters, all of the token groups)
+    (MX_DEEP, 400, pkg.PATH_TILED), (MX_DEEP, 600, pkg.PATH_TILED),
 ])
 def test_mxfp4_forward_matches_oracle(dev, shape, tokens, path):
     wl = li.Workload("mxfp4", shape, tokens)

@@ -59,6 +59,30 @@ def test_medium_both_tilings(dev, path, tokens):
     assert_parity(rep)
 
 
+# latent and expert widths of 1024: both bf16 expert GEMMs take the two-stage
+# LDS GEMM with 512 weight rows per tile (the down projection too), whose
+# expert tiles skip the MFMAs of 16-row token groups past their rows and
+# the copies of token rows past them
+DEEP = li.LayerShape(512, 1024, 16, 4, 1024, 512, 5.0)
+
+
+@pytest.mark.parametrize("tokens", [150, 400, 600])
+def test_expert_tiles_at_every_fill_level(dev, tokens):
+    """Tiled path with ~37, ~100 and ~150 rows per expert: 128-row expert
+    tiles whose row counts put the second wave row, and the last 16-row
+    token group, at every fill level; every token compared."""
+    wl = li.Workload("deep", DEEP, tokens)
+    say(f"[deep T={tokens} tiled]")
+    inp = li.make_inputs(wl, dev)
+    g = run_gpu(layer_for(wl, inp, pkg.PATH_TILED), inp.x)
+    check_properties(g, wl.shape, tokens)
+    counts = np.bincount(g.idx.ravel(), minlength=DEEP.n_routed_experts) % 128
+    say(f"  last-tile rows per expert: {sorted(set(counts.tolist()))}")
+    rep = compare(g, li.bf16_bits(inp.x), li.HostWeights(inp, eager_experts=True), wl.shape)
+    say(rep)
+    assert_parity(rep)
+
+
 @pytest.mark.parametrize("tokens", [64, 65, 256, 257])
 def test_dense_gemm_mode_boundaries(dev, tokens):
     """Automatic path at the token counts where the dense GEMMs switch from
