@@ -1142,11 +1142,11 @@ static hipError_t launch_expert(const P& p, const Tile* tiles, const int* ntiles
 
 // Expert up projection: lds_gemm_kernel when N allows 512-row weight tiles
 // and every gathered latent row lies within the 2 GiB its buffer offsets
-// reach (a row index is below the token count, which is at most the slot
-// count, itself below max_tiles * tile rows).
+// reach from the latent array's start (a row index is below the token
+// count).
 hipError_t tiled_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, int max_tiles,
-                        hipStream_t s) {
-  if (p.N() % 512 == 0 && p.K() % 128 == 0 && (long)max_tiles * kExpBM * p.K() * 2 < (1L << 31)) {
+                        int tokens, hipStream_t s) {
+  if (p.N() % 512 == 0 && p.K() % 128 == 0 && (long)tokens * p.K() * 2 < (1L << 31)) {
     const long grid = xcd_grid((long)max_tiles * (p.N() / 512));
     if (grid <= 0) return hipSuccess;
     lds_gemm_kernel<ExpUp, true, kExpBM, 512, 0><<<grid, 512, 0, s>>>(p, 0, tiles, ntiles);
@@ -1182,9 +1182,10 @@ static hipError_t launch_expert_mx(const P& p, const Tile* tiles, const int* nti
 // multiple of 512 (whole groups of four 128-k stages, whose 16 scale bytes
 // per row are then one aligned 16-byte piece), the scales 16-byte aligned,
 // and the token rows' byte offsets from the tile's first row within the
-// 2 GiB its buffer offsets reach: gathered rows (up projection) lie less than
-// the token count, itself at most the slot count (below max_tiles * tile
-// rows), rows after it; rows read in place (down projection) lie within the
+// 2 GiB its buffer offsets reach, which holds while `a_rows` rows do:
+// gathered rows (up projection; `a_rows` = the token count) are one expert's
+// tokens in ascending order, so they lie after the tile's first row by less
+// than the token count; rows read in place (down projection) lie within the
 // tile's 128.  Wave layout 1 x 8, whose 128 x 64 blocks go out through LDS
 // (staged_store).  Measured at the prefill batch (T = 8192, all three give the
 // same bits), with direct stores 1 x 8 took the down projection from 3.38 to
@@ -1192,8 +1193,8 @@ static hipError_t launch_expert_mx(const P& p, const Tile* tiles, const int* nti
 // ms for both layouts).
 template <class P>
 static hipError_t launch_lds_mx(const P& p, const Tile* tiles, const int* ntiles, int max_tiles,
-                                hipStream_t s) {
-  const long a_span = (P::kGatherA ? (long)max_tiles * kExpBM : (long)kExpBM) * p.K() * 2;
+                                long a_rows, hipStream_t s) {
+  const long a_span = a_rows * p.K() * 2;
   if (p.N() % 512 == 0 && p.K() % 512 == 0 && (reinterpret_cast<uintptr_t>(p.scales) & 15) == 0 &&
       a_span < (1L << 31)) {
     const long grid = xcd_grid((long)max_tiles * (p.N() / 512));
@@ -1205,12 +1206,12 @@ static hipError_t launch_lds_mx(const P& p, const Tile* tiles, const int* ntiles
 }
 
 hipError_t tiled_mx_exp_up(const ExpUpMx& p, const Tile* tiles, const int* ntiles, int max_tiles,
-                           hipStream_t s) {
-  return launch_lds_mx(p, tiles, ntiles, max_tiles, s);
+                           int tokens, hipStream_t s) {
+  return launch_lds_mx(p, tiles, ntiles, max_tiles, tokens, s);
 }
 hipError_t tiled_mx_exp_down(const ExpDownMx& p, const Tile* tiles, const int* ntiles,
                              int max_tiles, hipStream_t s) {
-  return launch_lds_mx(p, tiles, ntiles, max_tiles, s);
+  return launch_lds_mx(p, tiles, ntiles, max_tiles, kExpBM, s);
 }
 
 }  // namespace lmoe

@@ -31,8 +31,9 @@ constexpr int kStreamDenseMaxTokens = 64;
 // every N must be a multiple of tiled_block_n()).
 hipError_t tiled_proj_in(const ProjIn& p, hipStream_t s);
 hipError_t tiled_proj_out(const ProjOut& p, hipStream_t s);
+// tokens: the batch's token count (every gathered latent row index is below it)
 hipError_t tiled_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, int max_tiles,
-                        hipStream_t s);
+                        int tokens, hipStream_t s);
 hipError_t tiled_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles, int max_tiles,
                           hipStream_t s);
 int tiled_block_m();
@@ -52,15 +53,15 @@ hipError_t split_proj_out(const ProjOut& p, float* part, hipStream_t s);
 // expert GEMMs (K a multiple of 128, N a multiple of 64).
 hipError_t mxfp4_quantize(const uint16_t* w, long rows, int cols, uint8_t* codes,
                           uint8_t* scales, hipStream_t s);
-// rows_per_expert as for stream_exp_down
+// tokens as for tiled_exp_up, rows_per_expert as for stream_exp_down
 hipError_t stream_mx_exp_up(const ExpUpMx& p, const Tile* tiles, const int* ntiles,
-                            int max_tiles, int rows_per_expert, hipStream_t s);
+                            int max_tiles, int tokens, int rows_per_expert, hipStream_t s);
 hipError_t stream_mx_exp_down(const ExpDownMx& p, const Tile* tiles, const int* ntiles,
                               int max_tiles, hipStream_t s);
 // The LDS-tiled expert GEMMs with MXFP4 weights (large batches; same
 // dimension requirements and tile list as tiled_exp_up / tiled_exp_down).
 hipError_t tiled_mx_exp_up(const ExpUpMx& p, const Tile* tiles, const int* ntiles, int max_tiles,
-                           hipStream_t s);
+                           int tokens, hipStream_t s);
 hipError_t tiled_mx_exp_down(const ExpDownMx& p, const Tile* tiles, const int* ntiles,
                              int max_tiles, hipStream_t s);
 

@@ -356,13 +356,13 @@ lmoe_status run_forward(const lmoe_config& c, const lmoe_weights& w, const Layou
   if (!mark()) return LMOE_ERR_HIP;
   if (mxfp4) {
     ExpUpMx pup{z16, rows_tok, w.expert_up_mxfp4, w.expert_up_scale, H, R, F};
-    if (!ok(expert_tiled ? tiled_mx_exp_up(pup, tiles, ntiles, ntile_max, s)
-                         : stream_mx_exp_up(pup, tiles, ntiles, ntile_max,
+    if (!ok(expert_tiled ? tiled_mx_exp_up(pup, tiles, ntiles, ntile_max, T, s)
+                         : stream_mx_exp_up(pup, tiles, ntiles, ntile_max, T,
                                             static_cast<int>((T * K + E - 1) / E), s)))
       return LMOE_ERR_HIP;
   } else {
     ExpUp pup{z16, rows_tok, w.expert_up, H, R, F};
-    if (!ok(expert_tiled ? tiled_exp_up(pup, tiles, ntiles, ntile_max, s)
+    if (!ok(expert_tiled ? tiled_exp_up(pup, tiles, ntiles, ntile_max, T, s)
                          : stream_exp_up(pup, tiles, ntiles, ntile_max, s)))
       return LMOE_ERR_HIP;
   }

@@ -352,9 +352,10 @@ __global__ __launch_bounds__(NW * 64) void stream_mx_lds_kernel(P p, const Tile*
 
 // stream_mx_lds_kernel where its conditions hold (K a multiple of 512, N of
 // 128, codes and scales 16-byte aligned, and the token rows' byte offsets
-// from a tile's first row within the 2 GiB of a buffer descriptor: gathered
-// rows lie less than the token count, at most the slot count, itself at most
-// max_tiles * 16, rows after it; rows read in place lie within the tile's 16);
+// from a tile's first row within the 2 GiB of a buffer descriptor, which
+// holds while `a_rows` rows do: gathered rows (`a_rows` = the token count) are
+// one expert's tokens in ascending order, so they lie after the first by less
+// than the token count; rows read in place lie within the tile's 16);
 // otherwise the general kernel with the largest of 4, 2, 1 waves per
 // work-group whose k share is a whole number of 128-k steps (K is a multiple
 // of 128).
@@ -366,9 +367,9 @@ __global__ __launch_bounds__(NW * 64) void stream_mx_lds_kernel(P p, const Tile*
 // with two, 337 / 472 with four; eight waves of two or four were no better.
 template <class P>
 static hipError_t launch_mx(const P& p, const Tile* tiles, const int* ntiles, int max_tiles,
-                            bool wide, hipStream_t s) {
+                            long a_rows, bool wide, hipStream_t s) {
   const bool aligned = ((reinterpret_cast<uintptr_t>(p.codes) | reinterpret_cast<uintptr_t>(p.scales)) & 15) == 0;
-  const long a_span = (P::kGatherA ? (long)max_tiles * 16 : 16L) * p.K() * 2;
+  const long a_span = a_rows * p.K() * 2;
   if (p.K() % 512 == 0 && p.N() % 128 == 0 && aligned && a_span < (1L << 31)) {
     if (wide && p.N() % 256 == 0) {
       const long grid = (long)max_tiles * (p.N() / 256);
@@ -394,12 +395,12 @@ static hipError_t launch_mx(const P& p, const Tile* tiles, const int* ntiles, in
 }
 
 hipError_t stream_mx_exp_up(const ExpUpMx& p, const Tile* tiles, const int* ntiles,
-                            int max_tiles, int rows_per_expert, hipStream_t s) {
-  return launch_mx(p, tiles, ntiles, max_tiles, rows_per_expert > 2, s);
+                            int max_tiles, int tokens, int rows_per_expert, hipStream_t s) {
+  return launch_mx(p, tiles, ntiles, max_tiles, tokens, rows_per_expert > 2, s);
 }
 hipError_t stream_mx_exp_down(const ExpDownMx& p, const Tile* tiles, const int* ntiles,
                               int max_tiles, hipStream_t s) {
-  return launch_mx(p, tiles, ntiles, max_tiles, false, s);
+  return launch_mx(p, tiles, ntiles, max_tiles, 16, false, s);
 }
 
 }  // namespace lmoe

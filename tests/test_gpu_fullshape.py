@@ -8,7 +8,10 @@ configuration the benchmark times:
 * the whole layer output is compared with the oracle on a seeded sample of
   tokens plus every tie token (whose oracle output is re-evaluated on the
   GPU's selection); the layer is token-wise, so a row's oracle output needs
-  only that row."""
+  only that row.
+The long prefill batch (21504 tokens) gives a tile list of more than 4096
+tiles and an expert-sorted hidden array of more than 2 GiB (473088 rows of
+5120 bf16 values)."""
 
 import sys
 
@@ -44,10 +47,12 @@ def sample_rows(T, seed):
     return np.array(sorted(rows))
 
 
-@pytest.mark.parametrize("name", ["decode", "mtp_verify", "prefill", "skewed", "decode_grouped"])
-def test_full_shape(full, name):
+@pytest.mark.parametrize("name,tokens", [("decode", None), ("mtp_verify", None), ("prefill", None),
+                                         ("skewed", None), ("decode_grouped", None),
+                                         ("prefill", 21504)])
+def test_full_shape(full, name, tokens):
     dev, w = full
-    wl = li.workload(name)
+    wl = li.workload(name) if tokens is None else li.workload(name, tokens=tokens)
     print(f"[full {name} T={wl.tokens}]", flush=True)
     weights = dict(w)
     if wl.bias_recipe == "zipf":

@@ -134,15 +134,18 @@ def test_mxfp4_forward_matches_oracle(dev, shape, tokens, path):
 
 
 @pytest.mark.fullshape
-@pytest.mark.parametrize("name,rows", [("decode", [0, 13, 31]), ("prefill", [0, 4097, 8191])])
-def test_mxfp4_full_shape(dev, name, rows):
+@pytest.mark.parametrize("name,tokens,rows", [("decode", None, [0, 13, 31]),
+                                              ("prefill", None, [0, 4097, 8191]),
+                                              ("prefill", 21504, [0, 10752, 21503])])
+def test_mxfp4_full_shape(dev, name, tokens, rows):
     """The decode batch (weight streaming) and the prefill batch (LDS-tiled
-    MXFP4 GEMMs) at full shape with MXFP4 experts: properties on every
+    MXFP4 GEMMs) at full shape with MXFP4 experts, and a long prefill batch
+    of 21504 tokens (more than 4096 expert tiles): properties on every
     token, every token's routing against the oracle's, the whole output on
     three sampled tokens plus any tie token (every expert they use quantised
     by the oracle and compared with the library's codes)."""
-    wl = li.workload(name)
-    say(f"[mxfp4 full {name}]")
+    wl = li.workload(name) if tokens is None else li.workload(name, tokens=tokens)
+    say(f"[mxfp4 full {name} T={wl.tokens}]")
     inp = li.make_inputs(wl, dev)
     w = mx_weights(inp)
     layer = pkg.LatentMoE(wl.shape, w, wl.tokens, expert_format=pkg.EXPERTS_MXFP4)
