@@ -83,6 +83,27 @@ def test_expert_tiles_at_every_fill_level(dev, tokens):
     assert_parity(rep)
 
 
+# expert width 768 (a multiple of 256, not of 512) and latent 256: both
+# expert GEMMs take the three-stage tiled kernel with 256 weight rows per
+# tile, the up projection with gathered token rows
+NARROW = li.LayerShape(512, 256, 16, 4, 768, 512, 5.0)
+
+
+@pytest.mark.parametrize("tokens", [300, 700])
+def test_expert_widths_off_the_wide_tiles(dev, tokens):
+    """Tiled path where no expert width is a multiple of 512 (~75 and ~175
+    rows per expert: one partly filled tile, then a full one and a partly
+    filled one); every token compared."""
+    wl = li.Workload("narrow", NARROW, tokens)
+    say(f"[narrow T={tokens} tiled]")
+    inp = li.make_inputs(wl, dev)
+    g = run_gpu(layer_for(wl, inp, pkg.PATH_TILED), inp.x)
+    check_properties(g, wl.shape, tokens)
+    rep = compare(g, li.bf16_bits(inp.x), li.HostWeights(inp, eager_experts=True), wl.shape)
+    say(rep)
+    assert_parity(rep)
+
+
 @pytest.mark.parametrize("tokens", [64, 65, 256, 257])
 def test_dense_gemm_mode_boundaries(dev, tokens):
     """Automatic path at the token counts where the dense GEMMs switch from
