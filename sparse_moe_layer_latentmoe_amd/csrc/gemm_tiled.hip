@@ -647,6 +647,194 @@ __global__ __launch_bounds__(512) void lds_gemm_kernel(P p, int mrows, const Til
   lds_gemm_body<P, GROUPED, BM, BN, TwoSegments<P>::value ? 0 : SCHED>(p, mrows, tiles, ntiles);
 }
 
+// Grouped expert GEMM, bf16 weights, large batches: the 128 x 512 tile and
+// the 2 x 4 wave layout of lds_gemm_body, with the copies in half-steps.
+// Half-step s = 2 kt + h multiplies k tile kt of the token rows with weight
+// rows 256 h .. 256 h + 255 of the block; each wave owns 64 token rows x 64
+// weight rows of each half (128 weight rows in all, as in lds_gemm_body, in
+// two pieces).  The copy unit of half-step s is weight half h of k tile kt,
+// plus kt's token rows when h = 0.  Units are issued L half-steps ahead into
+// a ring of L + 1 weight-half buffers (32 KB) and two token buffers (16 KB),
+// so the wait at the top of a half-step leaves the next L - 1 units in
+// flight: the copy stream never drains, where one 80 KB stage ahead drained
+// it at every k tile.  Token fragments are read at h = 0 and kept in
+// registers for h = 1.  Each output element sees the MFMAs in the order of
+// lds_gemm_body (k tiles ascending, k halves 0 then 1), so the bits match.
+// Every wave copies its token rows whole (no skip of rows past the tile's
+// count): the wait counts below assume a fixed number of copies per unit.
+template <class P, int L>
+__device__ __forceinline__ void lds_pipe_body(const P& p, const Tile* tiles, const int* ntiles) {
+  constexpr int BM = 128, BN = 512, BH = 256, WM = 2, WN = 4, NW = WM * WN, BK = 64;
+  constexpr int TM = BM / WM / 16, TH = BH / WN / 16;
+  constexpr int RPI = 8, ROWB = BK * 2;
+  constexpr int NIA = BM / RPI / NW, NIH = BH / RPI / NW;
+  constexpr int ABUF = BM * ROWB, HBUF = BH * ROWB, NB = L + 1;
+  static_assert(L == 2 || L == 3, "lookahead");
+  static_assert(2 * ABUF + NB * HBUF <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * ABUF + NB * HBUF];
+
+  int tm, nb;
+  if (!work_item_uniform<true>(p.N() / BN, 0, BM, tiles, ntiles, tm, nb)) return;
+  const int e = uniform(tiles[tm].expert);
+  const int m0 = uniform(tiles[tm].row0);
+  const int mcount = uniform(tiles[tm].nrows);
+  const int n0 = nb * BN;
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const int wm = w / WN, wn = w % WN;
+  const int nsub = 2 * (p.K() / BK);
+
+  // copy sources as in lds_gemm_body: instruction j of wave w fills rows
+  // RPI (w + NW j) .. + 7 of its buffer, already swizzled
+  const int lr = lane >> 3;
+  const int sw = ((4 * (w & 1)) + (lr >> 1)) & 7;
+  const uint32_t chunk = (uint32_t)(((lane & 7) ^ sw) * 16);
+  const char* pa = reinterpret_cast<const char*>(P::kGatherA ? p.a_base0() : p.a_row0(m0));
+  uint32_t ao[NIA];
+#pragma unroll
+  for (int j = 0; j < NIA; ++j) {
+    const int row = RPI * (w + NW * j) + lr;
+    const int m = m0 + (row < mcount ? row : 0);
+    ao[j] = (uint32_t)(reinterpret_cast<const char*>(p.a_row0(m)) - pa) + chunk;
+  }
+  const char* pb = reinterpret_cast<const char*>(p.b_row0(e, n0));
+  const int ldb = (int)p.ldb0() * 2;
+  const uint32_t bo = (uint32_t)(lr * ldb) + chunk;
+  const int b0 = RPI * w * ldb, bstep = RPI * NW * ldb, bhalf = BH * ldb;
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(pa), rb = buffer_rsrc(pb);
+  char* const sa0 = smem;
+  char* const sb0 = smem + 2 * ABUF;
+
+  // issue copy unit u (its half H = u % 2 known here)
+  auto issue = [&](auto h_c, int u) __attribute__((always_inline)) {
+    constexpr int H = decltype(h_c)::value;
+    const int kb = (u >> 1) * ROWB;
+    if constexpr (H == 0) {
+      char* st = sa0 + ((u >> 1) & 1) * ABUF;
+#pragma unroll
+      for (int j = 0; j < NIA; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + (w + NW * j) * RPI * ROWB),
+                                                 16, ao[j], kb, 0, 0);
+    }
+    char* st = sb0 + (u % NB) * HBUF;
+#pragma unroll
+    for (int j = 0; j < NIH; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + (w + NW * j) * RPI * ROWB), 16,
+                                               bo, kb + b0 + j * bstep + H * bhalf, 0, 0);
+  };
+  // wait until unit s has landed: the later units in flight are s + 1 ..
+  // min(s + L - 1, nsub - 1), NIH copies each plus NIA for even ones
+  auto wait_unit = [&](auto h_c, int s) __attribute__((always_inline)) {
+    constexpr int H = decltype(h_c)::value;
+    if constexpr (L == 3) {
+      if (s + 2 < nsub) wait_vmcnt<2 * NIH + NIA>();
+      else if (H == 0 && s + 1 < nsub) wait_vmcnt<NIH>();
+      else wait_vmcnt<0>();
+    } else {
+      if (s + 1 < nsub) wait_vmcnt<H == 0 ? NIH : NIH + NIA>();
+      else wait_vmcnt<0>();
+    }
+  };
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, 1>;
+  using HL0 = std::integral_constant<int, (L & 1)>;      // half of unit s + L, s even
+  using HL1 = std::integral_constant<int, (L & 1) ^ 1>;  // s odd
+
+#pragma unroll
+  for (int u = 0; u < L; ++u) {
+    if (u & 1) issue(H1{}, u);
+    else issue(H0{}, u);
+  }
+
+  const int r16 = lane & 15, kq = lane >> 4;
+  const uint32_t l0 = r16 * ROWB + (((0 + kq) ^ (r16 >> 1)) << 4);
+  const uint32_t l1 = r16 * ROWB + (((4 + kq) ^ (r16 >> 1)) << 4);
+  const uint32_t aw = (uint32_t)(wm * (BM / WM)) * ROWB;
+  const uint32_t bw = (uint32_t)(wn * (BH / WN)) * ROWB;
+  const bool has_rows = wm * (BM / WM) < mcount;
+  const int tlim = uniform(min(TM, max(0, (mcount - wm * (BM / WM) + 15) / 16)));
+
+  if (!has_rows) {
+    // every token row of this wave lies past the tile's count: it only copies
+    for (int s = 0; s < nsub; s += 2) {
+      wait_unit(H0{}, s);
+      stage_barrier_hard();
+      if (s + L < nsub) issue(HL0{}, s + L);
+      wait_unit(H1{}, s + 1);
+      stage_barrier_hard();
+      if (s + 1 + L < nsub) issue(HL1{}, s + 1 + L);
+    }
+    return;
+  }
+
+  f32x4 acc[2 * TH][TM];
+#pragma unroll
+  for (int a = 0; a < 2 * TH; ++a)
+#pragma unroll
+    for (int b = 0; b < TM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 xf[2][TM];  // token fragments of the current k tile
+
+  auto half_step = [&](auto h_c, auto hl_c, int s) __attribute__((always_inline)) {
+    constexpr int H = decltype(h_c)::value;
+    wait_unit(h_c, s);
+    stage_barrier_hard();
+    if (s + L < nsub) issue(hl_c, s + L);
+    if constexpr (H == 0) {
+      const char* st = sa0 + ((s >> 1) & 1) * ABUF + aw;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+          xf[ks][t] = *reinterpret_cast<const bf16x8*>(st + (ks ? l1 : l0) + t * 16 * ROWB);
+    }
+    const char* st = sb0 + (s % NB) * HBUF + bw;
+    bf16x8 wf[2][TH];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int g = 0; g < TH; ++g)
+        wf[ks][g] = *reinterpret_cast<const bf16x8*>(st + (ks ? l1 : l0) + g * 16 * ROWB);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int t = 0; t < TM; ++t)
+        if (t < tlim)
+#pragma unroll
+          for (int g = 0; g < TH; ++g)
+            acc[H * TH + g][t] = mfma_bf16(wf[ks][g], xf[ks][t], acc[H * TH + g][t]);
+  };
+  for (int s = 0; s < nsub; s += 2) {
+    half_step(H0{}, HL0{}, s);
+    half_step(H1{}, HL1{}, s + 1);
+  }
+
+  const int wr = wm * (BM / WM);
+  if constexpr (P::kStagedStore) {
+    // through LDS away from the weight-half buffer of the last half-step:
+    // every wave passed that half-step's barrier, so every other buffer's
+    // last reader is done, and every copy has landed (vmcnt(0) above)
+    const int last = (nsub - 1) % NB;
+    char* const reg = smem + (last == 0 ? 2 * ABUF + HBUF : 0) + w * (64 * 128);
+    staged_store<4, 0>(p, reg, lane, acc, m0 + wr, mcount - wr, n0 + wn * (BH / WN));
+    staged_store<4, 4>(p, reg, lane, acc, m0 + wr, mcount - wr, n0 + BH + wn * (BH / WN));
+    return;
+  }
+  const int ncol = (lane >> 4) * 4;
+#pragma unroll
+  for (int g = 0; g < 2 * TH; ++g)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      const int i = wr + t * 16 + r16;
+      const int n = n0 + (g / TH) * BH + wn * (BH / WN) + (g % TH) * 16 + ncol;
+      if (i < mcount) p.store(e, m0 + i, n, acc[g][t]);
+    }
+}
+
+template <class P, int L>
+__global__ __launch_bounds__(512) void lds_pipe_kernel(P p, const Tile* tiles, const int* ntiles) {
+  lds_pipe_body<P, L>(p, tiles, ntiles);
+}
+
 // Grouped expert GEMM with MXFP4 weights for large batches: the main loop of
 // tiled_gemm_kernel (NS = 2 stages of 64 k), with each stage's weight rows
 // decoded from FP4 codes instead of copied.  Every lane owns whole 32-k code
@@ -1154,14 +1342,19 @@ hipError_t tiled_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, in
   }
   return launch_expert(p, tiles, ntiles, max_tiles, s);
 }
-// Expert down projection: lds_gemm_kernel too when N allows 512-row weight
-// tiles (its token rows are read in place, within the tile's 128).
+// Expert down projection: the half-step kernel (lds_pipe_kernel, three
+// units ahead) when N allows 512-row weight tiles (its token rows are read in
+// place, within the tile's 128).  Measured on the prefill and skewed batches
+// against lds_gemm_kernel on one box, same bits: 4.20-4.26 against 4.42-4.59
+// ms (two units ahead: 4.32).  The up projection (32 k tiles of 2048 against
+// the down projection's 80) was slower on it, 4.51-4.66 against 4.49-4.51
+// ms, and keeps lds_gemm_kernel.
 hipError_t tiled_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles, int max_tiles,
                           hipStream_t s) {
   if (p.N() % 512 == 0 && p.K() % 128 == 0) {
     const long grid = xcd_grid((long)max_tiles * (p.N() / 512));
     if (grid <= 0) return hipSuccess;
-    lds_gemm_kernel<ExpDown, true, kExpBM, 512, 0><<<grid, 512, 0, s>>>(p, 0, tiles, ntiles);
+    lds_pipe_kernel<ExpDown, 3><<<grid, 512, 0, s>>>(p, tiles, ntiles);
     return hipGetLastError();
   }
   return launch_expert(p, tiles, ntiles, max_tiles, s);
