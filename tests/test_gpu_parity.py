@@ -59,10 +59,10 @@ def test_medium_both_tilings(dev, path, tokens):
     assert_parity(rep)
 
 
-# latent and expert widths of 1024: both bf16 expert GEMMs take the two-stage
-# LDS GEMM with 512 weight rows per tile (the down projection too), whose
-# expert tiles skip the MFMAs of 16-row token groups past their rows and
-# the copies of token rows past them
+# latent and expert widths of 1024: both bf16 expert GEMMs take 512 weight
+# rows per tile (the up projection the two-stage LDS GEMM, which skips the
+# copies of token rows past a tile's rows, the down projection the half-step
+# pipelined one); both skip the MFMAs of 16-row token groups past them
 DEEP = li.LayerShape(512, 1024, 16, 4, 1024, 512, 5.0)
 
 
@@ -78,6 +78,27 @@ def test_expert_tiles_at_every_fill_level(dev, tokens):
     check_properties(g, wl.shape, tokens)
     counts = np.bincount(g.idx.ravel(), minlength=DEEP.n_routed_experts) % 128
     say(f"  last-tile rows per expert: {sorted(set(counts.tolist()))}")
+    rep = compare(g, li.bf16_bits(inp.x), li.HostWeights(inp, eager_experts=True), wl.shape)
+    say(rep)
+    assert_parity(rep)
+
+
+# expert width 256 and latent 512: the down projection takes the half-step
+# pipelined kernel with the shortest k range the tiled path allows (256, so
+# eight half-steps: the three-unit prologue and both tail waits overlap)
+SHORT_K = li.LayerShape(512, 512, 16, 4, 256, 512, 5.0)
+
+
+@pytest.mark.parametrize("tokens", [150, 600])
+def test_shortest_k_range_of_the_half_step_kernel(dev, tokens):
+    """Tiled path, down projection over k = 256 in 512-row weight tiles
+    (~37 rows per expert, where the second wave row only copies, and ~150,
+    a full tile and a partly filled one); every token compared."""
+    wl = li.Workload("short_k", SHORT_K, tokens)
+    say(f"[short_k T={tokens} tiled]")
+    inp = li.make_inputs(wl, dev)
+    g = run_gpu(layer_for(wl, inp, pkg.PATH_TILED), inp.x)
+    check_properties(g, wl.shape, tokens)
     rep = compare(g, li.bf16_bits(inp.x), li.HostWeights(inp, eager_experts=True), wl.shape)
     say(rep)
     assert_parity(rep)
