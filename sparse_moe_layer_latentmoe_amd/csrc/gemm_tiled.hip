@@ -660,8 +660,14 @@ __global__ __launch_bounds__(512) void lds_gemm_kernel(P p, int mrows, const Til
 // it at every k tile.  Token fragments are read at h = 0 and kept in
 // registers for h = 1.  Each output element sees the MFMAs in the order of
 // lds_gemm_body (k tiles ascending, k halves 0 then 1), so the bits match.
-// Every wave copies its token rows whole (no skip of rows past the tile's
-// count): the wait counts below assume a fixed number of copies per unit.
+// Every wave copies its token rows whole (rows past the tile's count read
+// its first row): the wait counts below assume a fixed number of copies per
+// unit.  Every wave also runs all its MFMAs, those of token rows past the
+// count included (their outputs are not stored): measured on the prefill and
+// skewed batches, skipping the 16-row groups past the count made the down
+// projection 3% slower (4.28-4.36 against 4.15-4.24 ms, same bits), since
+// partly filled tiles then run ahead of the full tiles that share their
+// weight panel and stop meeting them in L2.
 template <class P, int L>
 __device__ __forceinline__ void lds_pipe_body(const P& p, const Tile* tiles, const int* ntiles) {
   constexpr int BM = 128, BN = 512, BH = 256, WM = 2, WN = 4, NW = WM * WN, BK = 64;
@@ -751,22 +757,6 @@ __device__ __forceinline__ void lds_pipe_body(const P& p, const Tile* tiles, con
   const uint32_t l1 = r16 * ROWB + (((4 + kq) ^ (r16 >> 1)) << 4);
   const uint32_t aw = (uint32_t)(wm * (BM / WM)) * ROWB;
   const uint32_t bw = (uint32_t)(wn * (BH / WN)) * ROWB;
-  const bool has_rows = wm * (BM / WM) < mcount;
-  const int tlim = uniform(min(TM, max(0, (mcount - wm * (BM / WM) + 15) / 16)));
-
-  if (!has_rows) {
-    // every token row of this wave lies past the tile's count: it only copies
-    for (int s = 0; s < nsub; s += 2) {
-      wait_unit(H0{}, s);
-      stage_barrier_hard();
-      if (s + L < nsub) issue(HL0{}, s + L);
-      wait_unit(H1{}, s + 1);
-      stage_barrier_hard();
-      if (s + 1 + L < nsub) issue(HL1{}, s + 1 + L);
-    }
-    return;
-  }
-
   f32x4 acc[2 * TH][TM];
 #pragma unroll
   for (int a = 0; a < 2 * TH; ++a)
@@ -798,10 +788,9 @@ __device__ __forceinline__ void lds_pipe_body(const P& p, const Tile* tiles, con
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int t = 0; t < TM; ++t)
-        if (t < tlim)
 #pragma unroll
-          for (int g = 0; g < TH; ++g)
-            acc[H * TH + g][t] = mfma_bf16(wf[ks][g], xf[ks][t], acc[H * TH + g][t]);
+        for (int g = 0; g < TH; ++g)
+          acc[H * TH + g][t] = mfma_bf16(wf[ks][g], xf[ks][t], acc[H * TH + g][t]);
   };
   for (int s = 0; s < nsub; s += 2) {
     half_step(H0{}, HL0{}, s);
@@ -810,7 +799,8 @@ __device__ __forceinline__ void lds_pipe_body(const P& p, const Tile* tiles, con
 
   const int wr = wm * (BM / WM);
   if constexpr (P::kStagedStore) {
-    // through LDS away from the weight-half buffer of the last half-step:
+    // through LDS away from the weight-half buffer of the last half-step
+  // (rows past the tile's count are not stored):
     // every wave passed that half-step's barrier, so every other buffer's
     // last reader is done, and every copy has landed (vmcnt(0) above)
     const int last = (nsub - 1) % NB;
@@ -1346,9 +1336,10 @@ hipError_t tiled_exp_up(const ExpUp& p, const Tile* tiles, const int* ntiles, in
 // units ahead) when N allows 512-row weight tiles (its token rows are read in
 // place, within the tile's 128).  Measured on the prefill and skewed batches
 // against lds_gemm_kernel on one box, same bits: 4.20-4.26 against 4.42-4.59
-// ms (two units ahead: 4.32).  The up projection (32 k tiles of 2048 against
-// the down projection's 80) was slower on it, 4.51-4.66 against 4.49-4.51
-// ms, and keeps lds_gemm_kernel.
+// ms (two units ahead: 4.32), and 4.15-4.24 once it ran the MFMAs of partly
+// filled tiles' padding rows too.  The up projection (32 k tiles of 2048
+// against the down projection's 80) was slower on it either way, 4.51-4.66
+// against 4.47-4.53 ms, and keeps lds_gemm_kernel.
 hipError_t tiled_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles, int max_tiles,
                           hipStream_t s) {
   if (p.N() % 512 == 0 && p.K() % 128 == 0) {
