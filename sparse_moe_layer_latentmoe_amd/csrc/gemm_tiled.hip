@@ -16,7 +16,9 @@
 // the LDS rows are XOR-swizzled so the 16 rows of an MFMA fragment read
 // fall in distinct banks (measured: zero bank conflicts).  Each k tile: wait
 // for this tile's loads, one barrier, the next stage's loads, all fragment
-// reads, then the MFMAs.
+// reads, then the MFMAs.  lds_pipe_kernel (the whole-k dense projections and
+// the expert down projection) splits each k tile into two half-steps and
+// keeps two copy units in flight across the waits.
 //
 // Work order is XCD-aware (see work_item).  Grouped mode (experts) takes the
 // m tiles from the expert tile list built by the dispatch kernel; a tile
@@ -647,19 +649,21 @@ __global__ __launch_bounds__(512) void lds_gemm_kernel(P p, int mrows, const Til
   lds_gemm_body<P, GROUPED, BM, BN, TwoSegments<P>::value ? 0 : SCHED>(p, mrows, tiles, ntiles);
 }
 
-// Grouped expert GEMM, bf16 weights, large batches: the 128 x 512 tile and
-// the 2 x 4 wave layout of lds_gemm_body, with the copies in half-steps.
-// Half-step s = 2 kt + h multiplies k tile kt of the token rows with weight
-// rows 256 h .. 256 h + 255 of the block; each wave owns 64 token rows x 64
-// weight rows of each half (128 weight rows in all, as in lds_gemm_body, in
-// two pieces).  The copy unit of half-step s is weight half h of k tile kt,
-// plus kt's token rows when h = 0.  Units are issued L half-steps ahead into
-// a ring of L + 1 weight-half buffers (32 KB) and two token buffers (16 KB),
-// so the wait at the top of a half-step leaves the next L - 1 units in
-// flight: the copy stream never drains, where one 80 KB stage ahead drained
-// it at every k tile.  Token fragments are read at h = 0 and kept in
-// registers for h = 1.  Each output element sees the MFMAs in the order of
-// lds_gemm_body (k tiles ascending, k halves 0 then 1), so the bits match.
+// Half-step pipelined LDS GEMM: the tiles and the 2 x 4 wave layout of
+// lds_gemm_body (expert down projection: 128 x 512 tiles; whole-k dense
+// projections: 256 x 256, the output projection's two k segments included),
+// with the copies in half-steps.  Half-step s = 2 kt + h multiplies k tile kt
+// of the token rows with weight rows BN/2 h .. BN/2 h + BN/2 - 1 of the
+// block; each wave owns BM/2 token rows x BN/8 weight rows of each half
+// (BN/4 weight rows in all, as in lds_gemm_body, in two pieces).  The copy
+// unit of half-step s is weight half h of k tile kt, plus kt's token rows
+// when h = 0.  Units are issued L half-steps ahead into a ring of L + 1
+// weight-half buffers and two token buffers, so the wait at the top of a
+// half-step leaves the next L - 1 units in flight: the copy stream never
+// drains, where one stage ahead drained it at every k tile.  Token fragments
+// are read at h = 0 and kept in registers for h = 1.  Each output element
+// sees the MFMAs in the order of lds_gemm_body (k tiles ascending, k halves
+// 0 then 1), so the bits match.
 // Every wave copies its token rows whole (rows past the tile's count read
 // its first row): the wait counts below assume a fixed number of copies per
 // unit.  Every wave also runs all its MFMAs, those of token rows past the
@@ -668,65 +672,102 @@ __global__ __launch_bounds__(512) void lds_gemm_kernel(P p, int mrows, const Til
 // projection 3% slower (4.28-4.36 against 4.15-4.24 ms, same bits), since
 // partly filled tiles then run ahead of the full tiles that share their
 // weight panel and stop meeting them in L2.
-template <class P, int L>
-__device__ __forceinline__ void lds_pipe_body(const P& p, const Tile* tiles, const int* ntiles) {
-  constexpr int BM = 128, BN = 512, BH = 256, WM = 2, WN = 4, NW = WM * WN, BK = 64;
+template <class P, bool GROUPED, int BM, int BN, int L>
+__device__ __forceinline__ void lds_pipe_body(const P& p, int mrows, const Tile* tiles,
+                                              const int* ntiles) {
+  constexpr int BH = BN / 2, WM = 2, WN = 4, NW = WM * WN, BK = 64;
   constexpr int TM = BM / WM / 16, TH = BH / WN / 16;
   constexpr int RPI = 8, ROWB = BK * 2;
   constexpr int NIA = BM / RPI / NW, NIH = BH / RPI / NW;
   constexpr int ABUF = BM * ROWB, HBUF = BH * ROWB, NB = L + 1;
+  constexpr bool SEG2 = TwoSegments<P>::value;
+  static_assert(NIA * RPI * NW == BM && NIH * RPI * NW == BH, "rows per unit");
   static_assert(L == 2 || L == 3, "lookahead");
   static_assert(2 * ABUF + NB * HBUF <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(1024))) char smem[2 * ABUF + NB * HBUF];
 
   int tm, nb;
-  if (!work_item_uniform<true>(p.N() / BN, 0, BM, tiles, ntiles, tm, nb)) return;
-  const int e = uniform(tiles[tm].expert);
-  const int m0 = uniform(tiles[tm].row0);
-  const int mcount = uniform(tiles[tm].nrows);
+  if (!work_item_uniform<GROUPED>(p.N() / BN, mrows, BM, tiles, ntiles, tm, nb)) return;
+  int e = 0, m0, mcount;
+  if (GROUPED) {
+    e = uniform(tiles[tm].expert);
+    m0 = uniform(tiles[tm].row0);
+    mcount = uniform(tiles[tm].nrows);
+  } else {
+    m0 = tm * BM;
+    mcount = min(BM, mrows - m0);
+  }
   const int n0 = nb * BN;
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int wm = w / WN, wn = w % WN;
-  const int nsub = 2 * (p.K() / BK);
+  const int nk = p.K() / BK;
+  const int nk0 = SEG2 ? p.K0() / BK : nk;
+  const int nsub = 2 * nk;
 
-  // copy sources as in lds_gemm_body: instruction j of wave w fills rows
-  // RPI (w + NW j) .. + 7 of its buffer, already swizzled
+  // copy sources of one k segment, as in lds_gemm_body: instruction j of
+  // wave w fills rows RPI (w + NW j) .. + 7 of its buffer, already swizzled;
+  // token rows past the tile's count read its first row
   const int lr = lane >> 3;
   const int sw = ((4 * (w & 1)) + (lr >> 1)) & 7;
   const uint32_t chunk = (uint32_t)(((lane & 7) ^ sw) * 16);
-  const char* pa = reinterpret_cast<const char*>(P::kGatherA ? p.a_base0() : p.a_row0(m0));
-  uint32_t ao[NIA];
+  struct Seg {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    uint32_t ao[NIA];
+    uint32_t bo;
+    int b0, bstep, bhalf;
+  };
+  auto make_seg = [&](int seg) __attribute__((always_inline)) {
+    Seg g;
+    const char* pa = GROUPED && P::kGatherA
+                         ? reinterpret_cast<const char*>(seg ? p.a_base1() : p.a_base0())
+                         : reinterpret_cast<const char*>(seg ? p.a_row1(m0) : p.a_row0(m0));
 #pragma unroll
-  for (int j = 0; j < NIA; ++j) {
-    const int row = RPI * (w + NW * j) + lr;
-    const int m = m0 + (row < mcount ? row : 0);
-    ao[j] = (uint32_t)(reinterpret_cast<const char*>(p.a_row0(m)) - pa) + chunk;
-  }
-  const char* pb = reinterpret_cast<const char*>(p.b_row0(e, n0));
-  const int ldb = (int)p.ldb0() * 2;
-  const uint32_t bo = (uint32_t)(lr * ldb) + chunk;
-  const int b0 = RPI * w * ldb, bstep = RPI * NW * ldb, bhalf = BH * ldb;
-  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(pa), rb = buffer_rsrc(pb);
+    for (int j = 0; j < NIA; ++j) {
+      const int row = RPI * (w + NW * j) + lr;
+      const int m = m0 + (row < mcount ? row : 0);
+      g.ao[j] = (uint32_t)(reinterpret_cast<const char*>(seg ? p.a_row1(m) : p.a_row0(m)) - pa) +
+                chunk;
+    }
+    const char* pb = reinterpret_cast<const char*>(seg ? p.b_row1(e, n0) : p.b_row0(e, n0));
+    const int ldb = (int)(seg ? p.ldb1() : p.ldb0()) * 2;
+    g.bo = (uint32_t)(lr * ldb) + chunk;
+    g.b0 = RPI * w * ldb;
+    g.bstep = RPI * NW * ldb;
+    g.bhalf = BH * ldb;
+    g.ra = buffer_rsrc(pa);
+    g.rb = buffer_rsrc(pb);
+    return g;
+  };
+  const Seg g0 = make_seg(0);
+  const Seg g1 = SEG2 && nk0 < nk ? make_seg(1) : g0;
   char* const sa0 = smem;
   char* const sb0 = smem + 2 * ABUF;
 
-  // issue copy unit u (its half H = u % 2 known here)
-  auto issue = [&](auto h_c, int u) __attribute__((always_inline)) {
+  // issue copy unit u (its half H = u % 2 known here) from segment g, k
+  // tile kt at byte offset kb within that segment's rows
+  auto issue_seg = [&](auto h_c, const Seg& g, int u, int kb) __attribute__((always_inline)) {
     constexpr int H = decltype(h_c)::value;
-    const int kb = (u >> 1) * ROWB;
     if constexpr (H == 0) {
       char* st = sa0 + ((u >> 1) & 1) * ABUF;
 #pragma unroll
       for (int j = 0; j < NIA; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + (w + NW * j) * RPI * ROWB),
-                                                 16, ao[j], kb, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(g.ra, (lds_void*)(st + (w + NW * j) * RPI * ROWB),
+                                                 16, g.ao[j], kb, 0, 0);
     }
     char* st = sb0 + (u % NB) * HBUF;
 #pragma unroll
     for (int j = 0; j < NIH; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + (w + NW * j) * RPI * ROWB), 16,
-                                               bo, kb + b0 + j * bstep + H * bhalf, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g.rb, (lds_void*)(st + (w + NW * j) * RPI * ROWB),
+                                               16, g.bo, kb + g.b0 + j * g.bstep + H * g.bhalf, 0,
+                                               0);
+  };
+  // both segments issue the same copies, so the wait counts hold across the
+  // boundary
+  auto issue = [&](auto h_c, int u) __attribute__((always_inline)) {
+    const int kt = u >> 1;
+    if (SEG2 && kt >= nk0) issue_seg(h_c, g1, u, (kt - nk0) * ROWB);
+    else issue_seg(h_c, g0, u, kt * ROWB);
   };
   // wait until unit s has landed: the later units in flight are s + 1 ..
   // min(s + L - 1, nsub - 1), NIH copies each plus NIA for even ones
@@ -798,11 +839,11 @@ __device__ __forceinline__ void lds_pipe_body(const P& p, const Tile* tiles, con
   }
 
   const int wr = wm * (BM / WM);
-  if constexpr (P::kStagedStore) {
+  if constexpr (GROUPED && P::kStagedStore && TH == 4 && TM == 4) {
     // through LDS away from the weight-half buffer of the last half-step
-  // (rows past the tile's count are not stored):
-    // every wave passed that half-step's barrier, so every other buffer's
-    // last reader is done, and every copy has landed (vmcnt(0) above)
+    // (rows past the tile's count are not stored): every wave passed that
+    // half-step's barrier, so every other buffer's last reader is done, and
+    // every copy has landed (vmcnt(0) above)
     const int last = (nsub - 1) % NB;
     char* const reg = smem + (last == 0 ? 2 * ABUF + HBUF : 0) + w * (64 * 128);
     staged_store<4, 0>(p, reg, lane, acc, m0 + wr, mcount - wr, n0 + wn * (BH / WN));
@@ -820,9 +861,10 @@ __device__ __forceinline__ void lds_pipe_body(const P& p, const Tile* tiles, con
     }
 }
 
-template <class P, int L>
-__global__ __launch_bounds__(512) void lds_pipe_kernel(P p, const Tile* tiles, const int* ntiles) {
-  lds_pipe_body<P, L>(p, tiles, ntiles);
+template <class P, bool GROUPED, int BM, int BN, int L>
+__global__ __launch_bounds__(512) void lds_pipe_kernel(P p, int mrows, const Tile* tiles,
+                                                       const int* ntiles) {
+  lds_pipe_body<P, GROUPED, BM, BN, L>(p, mrows, tiles, ntiles);
 }
 
 // Grouped expert GEMM with MXFP4 weights for large batches: the main loop of
@@ -1219,8 +1261,12 @@ static hipError_t launch_dense(const P& p, int T, hipStream_t s) {
   const long grid = xcd_grid((long)((T + BM - 1) / BM) * (p.N() / BN));
   if (grid <= 0) return hipSuccess;
   static_assert(NS == 2 && BK == 64, "dense tiles");
+  // the half-step kernel, three units ahead: on the prefill batch (same bits)
+  // the output projection 1.463-1.468 -> 1.430-1.433 ms and the latent
+  // projection 0.245 -> 0.236 ms against lds_gemm_kernel, the forward
+  // 11.37-11.38 -> 11.29-11.30 ms (two A/B rounds on one box)
   if (p.K() % 128 == 0)
-    lds_gemm_kernel<P, false, BM, BN, 1><<<grid, 512, 0, s>>>(p, T, nullptr, nullptr);
+    lds_pipe_kernel<P, false, BM, BN, 3><<<grid, 512, 0, s>>>(p, T, nullptr, nullptr);
   else
     tiled_gemm_kernel<P, false, BM, BN, BK, NS, kWGN><<<grid, 128 * kWGN, 0, s>>>(p, T, nullptr,
                                                                                   nullptr);
@@ -1345,7 +1391,7 @@ hipError_t tiled_exp_down(const ExpDown& p, const Tile* tiles, const int* ntiles
   if (p.N() % 512 == 0 && p.K() % 128 == 0) {
     const long grid = xcd_grid((long)max_tiles * (p.N() / 512));
     if (grid <= 0) return hipSuccess;
-    lds_pipe_kernel<ExpDown, 3><<<grid, 512, 0, s>>>(p, tiles, ntiles);
+    lds_pipe_kernel<ExpDown, true, kExpBM, 512, 3><<<grid, 512, 0, s>>>(p, 0, tiles, ntiles);
     return hipGetLastError();
   }
   return launch_expert(p, tiles, ntiles, max_tiles, s);
