@@ -607,3 +607,42 @@ def test_planted_prenorm_mistakes_fail_the_pins(monkeypatch):
         with pytest.raises(AssertionError):
             test_prenorm_worked_rounding_and_factor()
     monkeypatch.setattr(O, "rms_prenorm", real)
+
+
+def _normalised_rows_are_scaled_not_rounded(block_forward):
+    """The pre-norm reading: the layer reads r_t * bf16(gamma * h_t) with the
+    factor r_t unrounded.  Both projections of the input are then exact
+    rescalings of the plain layer run on xt = bf16(gamma * h): the latent is
+    r_t times the plain latent (linear), and the shared expert's output is
+    r_t^2 times the plain one (relu^2 is homogeneous of degree 2).  Rounding
+    the normalised rows to bf16 instead perturbs both by up to 2^-9."""
+    x, w, cfg = tiny_inputs()
+    rng = np.random.default_rng(11)
+    h = li.bf16_bits(torch.from_numpy(3.0 * rng.standard_normal(x.shape).astype(np.float32)).to(torch.bfloat16))
+    g = li.bf16_bits(torch.from_numpy((1 + 0.1 * rng.standard_normal(x.shape[1])).astype(np.float32)).to(torch.bfloat16))
+    blk = block_forward(h, g, w, cfg, eps=1e-5)
+    rn = blk["rnorm"]
+    assert not np.any(np.isclose(np.log2(rn), np.round(np.log2(rn))))  # r is not a power of two
+    plain = O.forward(blk["xt"], w, cfg, forced_idx=blk["idx"])
+    np.testing.assert_allclose(blk["z"], rn[:, None] * plain["z"], rtol=1e-12,
+                               atol=1e-14 * np.abs(blk["z"]).max())
+    np.testing.assert_allclose(blk["y_shared"], rn[:, None] ** 2 * plain["y_shared"],
+                               rtol=1e-11, atol=1e-14 * np.abs(plain["y_shared"]).max())
+
+
+def test_prenorm_reading_keeps_the_factor_exact():
+    _normalised_rows_are_scaled_not_rounded(O.block_forward)
+
+
+def test_planted_rounded_normalised_rows_fail_the_reading_pin():
+    """The other reading (round r_t * gamma * h_t to bf16 before the layer)
+    fails the pin above."""
+    def rounded_rows(h_bits, gamma_bits, weights, cfg, eps=1e-5, residual=True, forced_idx=None):
+        xt, rn = O.rms_prenorm(h_bits, gamma_bits, eps)
+        rows = O.f32_to_bf16_bits((rn[:, None] * O.bf16_bits_to_f64(xt)).astype(np.float32))
+        out = O.layer(O.bf16_bits_to_f64(rows), weights, cfg, forced_idx)
+        out["xt"], out["rnorm"] = xt, rn
+        return out
+
+    with pytest.raises(AssertionError):
+        _normalised_rows_are_scaled_not_rounded(rounded_rows)
